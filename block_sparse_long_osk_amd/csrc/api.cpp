@@ -1,0 +1,217 @@
+// C-ABI entry points of libcosa_osk: host-side argument checks, workspace
+// sizing, and kernel launches on the caller's stream.  Declarations and the
+// contract of every function are in include/cosa_osk.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "cosa_osk.h"
+#include "osk_internal.h"
+
+namespace {
+
+using cosa_osk::kHeadDim;
+using cosa_osk::kPage;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool stride_ok(int64_t s) { return s > 0 && (s % 8) == 0; }
+
+cosa_status_t check_dims(const cosa_osk_dims_t* d) {
+  if (d == nullptr) return COSA_ERR_INVALID_ARG;
+  if (d->reserved != 0) return COSA_ERR_INVALID_ARG;
+  if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->total_q_tokens < 0 ||
+      d->total_qblocks < 0 || d->max_pages_per_seq < 1 || d->num_phys_pages < 0 || d->max_mask_len < 0)
+    return COSA_ERR_INVALID_ARG;
+  if (d->head_dim != kHeadDim || d->page_size != kPage) return COSA_ERR_UNSUPPORTED;
+  if (d->num_q_heads % d->num_kv_heads != 0) return COSA_ERR_UNSUPPORTED;
+  if (d->total_qblocks > cosa_osk::kMaxQBlocks || d->max_mask_len > cosa_osk::kMaxMaskLen ||
+      d->max_pages_per_seq > cosa_osk::kMaxPagesPerSeq)
+    return COSA_ERR_UNSUPPORTED;
+  // every query block holds 1..64 tokens
+  if ((int64_t)d->total_q_tokens > (int64_t)kPage * d->total_qblocks || d->total_qblocks > d->total_q_tokens)
+    return COSA_ERR_INVALID_ARG;
+  if (!stride_ok(d->q_stride_tok) || !stride_ok(d->q_stride_head) || !stride_ok(d->o_stride_tok) ||
+      !stride_ok(d->o_stride_head) || !stride_ok(d->kv_stride_page) || !stride_ok(d->kv_stride_head) ||
+      !stride_ok(d->kv_stride_tok))
+    return COSA_ERR_INVALID_ARG;
+  if (isnan(d->sm_scale) || isinf(d->sm_scale)) return COSA_ERR_INVALID_ARG;
+  return COSA_OK;
+}
+
+float resolved_scale(const cosa_osk_dims_t* d) {
+  return d->sm_scale > 0.f ? d->sm_scale : (float)(1.0 / sqrt((double)d->head_dim));
+}
+
+int keep_count(float b1, int n) {
+  if (n <= 0) return 0;
+  const int k = (int)ceil((double)b1 * (double)n - 1e-3);
+  return k < 0 ? 0 : (k > n ? n : k);
+}
+
+}  // namespace
+
+extern "C" {
+
+int cosa_abi_version(void) { return COSA_ABI_VERSION; }
+
+const char* cosa_status_string(cosa_status_t status) {
+  switch (status) {
+    case COSA_OK: return "ok";
+    case COSA_ERR_INVALID_ARG: return "invalid argument";
+    case COSA_ERR_UNSUPPORTED: return "unsupported shape or limit";
+    case COSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case COSA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t cosa_osk_workspace_bytes(const cosa_osk_dims_t* dims) {
+  if (dims == nullptr || dims->total_qblocks < 0) return 0;
+  return round_up((size_t)dims->total_qblocks * sizeof(int32_t) + 1);
+}
+
+cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_bytes) {
+  const cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  if (workspace_bytes < cosa_osk_workspace_bytes(dims)) return COSA_ERR_WORKSPACE;
+  return COSA_OK;
+}
+
+cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                               const int32_t* order_mask, const int32_t* mask_len, float budget2, void* out,
+                               float* lse, uint8_t* decisions, float* margins, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  cosa_status_t st = cosa_osk_check_args(dims, workspace_bytes);
+  if (st != COSA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr ||
+      cu_qblocks == nullptr || mask_len == nullptr || out == nullptr ||
+      (order_mask == nullptr && dims->max_mask_len > 0))
+    return COSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return COSA_ERR_INVALID_ARG;
+  if (margins != nullptr && decisions == nullptr) return COSA_ERR_INVALID_ARG;
+  if (isnan(budget2)) return COSA_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
+  cosa_osk::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_pool);
+  a.v = static_cast<const uint16_t*>(v_pool);
+  a.page_table = page_table;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_qblocks = cu_qblocks;
+  a.order_mask = order_mask;
+  a.mask_len = mask_len;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.decisions = decisions;
+  a.margins = margins;
+  a.sched = static_cast<int32_t*>(workspace);
+  a.q_st = dims->q_stride_tok;
+  a.q_sh = dims->q_stride_head;
+  a.o_st = dims->o_stride_tok;
+  a.o_sh = dims->o_stride_head;
+  a.kv_sp = dims->kv_stride_page;
+  a.kv_sh = dims->kv_stride_head;
+  a.kv_st = dims->kv_stride_tok;
+  a.num_seqs = dims->num_seqs;
+  a.hq = dims->num_q_heads;
+  a.hkv = dims->num_kv_heads;
+  a.total_qblocks = dims->total_qblocks;
+  a.max_pages = dims->max_pages_per_seq;
+  a.num_phys = dims->num_phys_pages;
+  a.max_mask_len = dims->max_mask_len;
+  a.sm_scale = resolved_scale(dims);
+  a.delta = budget2;
+  return cosa_osk::launch_prefill(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
+}
+
+int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t flags) {
+  if (max_pages_per_seq < 1) return -1;
+  int32_t width = 0;
+  for (int32_t i = 0; i < max_pages_per_seq; ++i) {
+    int nf = 0;
+    if (flags & COSA_FORCE_FIRST) ++nf;
+    if ((flags & COSA_FORCE_DIAG) && !((flags & COSA_FORCE_FIRST) && i == 0)) ++nf;
+    const int len = nf + keep_count(budget1, i + 1 - nf);
+    if (len > width) width = len;
+  }
+  return width;
+}
+
+size_t cosa_build_order_mask_workspace_bytes(const cosa_osk_dims_t* dims) {
+  if (dims == nullptr || dims->total_qblocks < 0 || dims->num_kv_heads < 1) return 0;
+  return 2 * round_up((size_t)dims->total_qblocks * dims->num_kv_heads * kHeadDim * sizeof(float) + 1);
+}
+
+cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                    const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                                    float budget1, uint32_t flags, int32_t* order_mask, int32_t* mask_len,
+                                    float* proxy_scores, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  if (dims->max_pages_per_seq > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
+  if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
+      order_mask == nullptr || mask_len == nullptr)
+    return COSA_ERR_INVALID_ARG;
+  if (!(budget1 >= 0.f && budget1 <= 1.f)) return COSA_ERR_INVALID_ARG;
+  if ((flags & ~(uint32_t)(COSA_FORCE_FIRST | COSA_FORCE_DIAG)) != 0u) return COSA_ERR_INVALID_ARG;
+  if (dims->max_mask_len < cosa_order_mask_width(dims->max_pages_per_seq, budget1, flags)) return COSA_ERR_INVALID_ARG;
+  const size_t need = cosa_build_order_mask_workspace_bytes(dims);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
+  cosa_osk::BuilderArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_pool);
+  a.page_table = page_table;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_qblocks = cu_qblocks;
+  a.order_mask = order_mask;
+  a.mask_len = mask_len;
+  a.scores = proxy_scores;
+  a.qbar = static_cast<float*>(workspace);
+  a.kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  a.q_st = dims->q_stride_tok;
+  a.q_sh = dims->q_stride_head;
+  a.kv_sp = dims->kv_stride_page;
+  a.kv_sh = dims->kv_stride_head;
+  a.kv_st = dims->kv_stride_tok;
+  a.num_seqs = dims->num_seqs;
+  a.hq = dims->num_q_heads;
+  a.hkv = dims->num_kv_heads;
+  a.total_qblocks = dims->total_qblocks;
+  a.max_pages = dims->max_pages_per_seq;
+  a.num_phys = dims->num_phys_pages;
+  a.max_mask_len = dims->max_mask_len;
+  a.budget1 = budget1;
+  a.flags = flags;
+  return cosa_osk::launch_build_order_mask(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
+}
+
+cosa_status_t cosa_validate_order_mask(const cosa_osk_dims_t* dims, const int32_t* page_table,
+                                       const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                                       const int32_t* order_mask, const int32_t* mask_len, int32_t* bad_counts,
+                                       hipStream_t stream) {
+  cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  if (page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr || mask_len == nullptr ||
+      bad_counts == nullptr || (order_mask == nullptr && dims->max_mask_len > 0))
+    return COSA_ERR_INVALID_ARG;
+  cosa_osk::ValidateArgs a;
+  a.page_table = page_table;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_qblocks = cu_qblocks;
+  a.order_mask = order_mask;
+  a.mask_len = mask_len;
+  a.bad = bad_counts;
+  a.num_seqs = dims->num_seqs;
+  a.hkv = dims->num_kv_heads;
+  a.total_qblocks = dims->total_qblocks;
+  a.max_pages = dims->max_pages_per_seq;
+  a.num_phys = dims->num_phys_pages;
+  a.max_mask_len = dims->max_mask_len;
+  return cosa_osk::launch_validate(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// Computation-order mask from the mean-pooled q.k proxy, for gfx950.
+//
+// Mask format: CoSA section 4.2, Eq. (14) -- row i lists the kept logical page
+// ids in visit order, -1 after them.  Proxy: the dot product of mean-pooled
+// query-block and key-page representations, kept pages visited in descending
+// proxy order (the CoSA rewrite page, section 4.2 "Implementation").  Grouped
+// q heads share one page set per KV head (PageWeaver notes, section 2), so the
+// query representation of KV head g sums the group's per-head block means.
+//
+// Kernels:
+//   pool   one workgroup per (query block, KV head), one thread per dim:
+//          qbar = sum_h mean_r q, kbar = mean_t k of the same-index logical page;
+//          Q and K are each read once, coalesced along the head dimension.
+//   select one workgroup per (query block, KV head): fp32 scores for the causal
+//          pages, forced pages set aside, a bitonic sort of the rest by
+//          (score desc, id asc) in LDS, and a merge of the forced pages into the
+//          top n_keep by the same key.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "osk_internal.h"
+
+namespace cosa_osk {
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ int seq_of_qblock(const int32_t* cu_qblocks, int num_seqs, int qb) {
+  int lo = 0, hi = num_seqs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu_qblocks[mid] <= qb) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(128) void mask_pool_kernel(const BuilderArgs a) {
+  const int qb = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
+  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
+  const int i = qb - a.cu_qblocks[s];
+  const int tok0 = a.cu_seqlens[s];
+  const int L = a.cu_seqlens[s + 1] - tok0;
+  const int rows = min(kPage, L - i * kPage);
+  const int G = a.hq / a.hkv;
+  float acc = 0.f;
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    float sh = 0.f;
+    for (int r = 0; r < rows; ++r)
+      sh += bf16_bits_to_float(a.q[(int64_t)(tok0 + i * kPage + r) * a.q_st + (int64_t)h * a.q_sh + d]);
+    acc += sh / (float)rows;
+  }
+  a.qbar[((int64_t)qb * a.hkv + g) * kHeadDim + d] = acc;
+  const int ph = i < a.max_pages ? a.page_table[(int64_t)s * a.max_pages + i] : -1;
+  float ks = 0.f;
+  if (ph >= 0 && ph < a.num_phys) {
+    const uint16_t* kp = a.k + (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + d;
+    for (int t = 0; t < rows; ++t) ks += bf16_bits_to_float(kp[(int64_t)t * a.kv_st]);
+    ks /= (float)rows;
+  }
+  a.kbar[((int64_t)qb * a.hkv + g) * kHeadDim + d] = ks;
+}
+
+// ceil(b1 * n - 1e-3) clamped to [0, n]
+__device__ __forceinline__ int keep_count(float b1, int n) {
+  if (n <= 0) return 0;
+  const int k = (int)ceil((double)b1 * (double)n - 1e-3);
+  return max(0, min(n, k));
+}
+
+// ascending key == (score descending, id ascending)
+__device__ __forceinline__ uint64_t sort_key(float score, int id) {
+  const uint32_t b = __float_as_uint(score);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // increasing in score
+  return ((uint64_t)(~ord) << 32) | (uint32_t)id;
+}
+
+__global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
+  __shared__ float qs[kHeadDim];
+  __shared__ uint64_t keys[kMaxPagesBuilder];
+  __shared__ uint64_t fkeys[2];
+  const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
+  // block index within the sequence; the clamp keeps the candidate list inside the
+  // LDS key array even for a cu_qblocks inconsistent with max_pages_per_seq
+  const int i = min(qb - a.cu_qblocks[s], a.max_pages - 1);
+  const int qb0 = a.cu_qblocks[s];
+  if (tid < kHeadDim) qs[tid] = a.qbar[((int64_t)qb * a.hkv + g) * kHeadDim + tid];
+  const bool f_first = (a.flags & 1u) != 0u;
+  const bool f_diag = (a.flags & 2u) != 0u && !(f_first && i == 0);
+  const int nf = (f_first ? 1 : 0) + (f_diag ? 1 : 0);
+  const int nrest = i + 1 - nf;
+  const int nkeep = keep_count(a.budget1, nrest);
+  int N = 1;
+  while (N < nrest) N <<= 1;
+  __syncthreads();
+  for (int j = tid; j <= i; j += 256) {
+    const float* kb = a.kbar + ((int64_t)(qb0 + j) * a.hkv + g) * kHeadDim;
+    float sc = 0.f;
+    for (int d = 0; d < kHeadDim; d += 4) {
+      const float4 kv = *(const float4*)(kb + d);
+      sc = fmaf(qs[d], kv.x, sc);
+      sc = fmaf(qs[d + 1], kv.y, sc);
+      sc = fmaf(qs[d + 2], kv.z, sc);
+      sc = fmaf(qs[d + 3], kv.w, sc);
+    }
+    if (a.scores) a.scores[((int64_t)qb * a.hkv + g) * a.max_pages + j] = sc;
+    const uint64_t key = sort_key(sc, j);
+    if (f_first && j == 0) fkeys[0] = key;
+    else if (f_diag && j == i) fkeys[f_first ? 1 : 0] = key;
+    else keys[j - ((f_first && j > 0) ? 1 : 0)] = key;
+  }
+  if (a.scores)
+    for (int j = i + 1 + tid; j < a.max_pages; j += 256)
+      a.scores[((int64_t)qb * a.hkv + g) * a.max_pages + j] = __builtin_nanf("");
+  for (int x = nrest + tid; x < N; x += 256) keys[x] = ~0ull;
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int kk = 2; kk <= N; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = tid; x < N; x += 256) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const uint64_t p = keys[x], q = keys[y];
+          const bool up = (x & kk) == 0;
+          if ((p > q) == up) { keys[x] = q; keys[y] = p; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // merge the forced pages into the top nkeep
+  int32_t* row = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
+  uint64_t fk[2] = {nf > 0 ? fkeys[0] : ~0ull, nf > 1 ? fkeys[1] : ~0ull};
+  for (int x = tid; x < nkeep; x += 256) {
+    const uint64_t kx = keys[x];
+    int before = 0;
+    for (int f = 0; f < nf; ++f) before += (fk[f] < kx) ? 1 : 0;
+    row[x + before] = (int32_t)(kx & 0xffffffffu);
+  }
+  if (tid < nf) {
+    const uint64_t kx = fk[tid];
+    int lo = 0, hi = nkeep;  // number of selected keys below kx
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (keys[mid] < kx) lo = mid + 1; else hi = mid;
+    }
+    const int other = (nf == 2 && fk[1 - tid] < kx) ? 1 : 0;
+    row[lo + other] = (int32_t)(kx & 0xffffffffu);
+  }
+  for (int x = nf + nkeep + tid; x < a.max_mask_len; x += 256) row[x] = -1;
+  if (tid == 0) a.mask_len[(int64_t)qb * a.hkv + g] = nf + nkeep;
+}
+
+hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream) {
+  if (a.total_qblocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.total_qblocks, (unsigned)a.hkv);
+  hipLaunchKernelGGL(mask_pool_kernel, grid, dim3(kHeadDim), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mask_select_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// validator: counts malformed mask entries (they are not visited by the prefill)
+// ---------------------------------------------------------------------------
+__global__ void zero_counts_kernel(int32_t* c, int n) {
+  if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(64) void validate_kernel(const ValidateArgs a) {
+  __shared__ uint32_t seen[kMaxPagesPerSeq / 32];
+  const int qb = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
+  const int i = qb - a.cu_qblocks[s];
+  const int L = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
+  const int n_pages = min((L + kPage - 1) / kPage, a.max_pages);
+  int len = a.mask_len[(int64_t)qb * a.hkv + g];
+  int c_range = 0, c_causal = 0, c_dup = 0, c_len = 0, c_phys = 0;
+  if (len < 0 || len > a.max_mask_len) {
+    c_len = lane == 0 ? 1 : 0;
+    len = min(max(len, 0), a.max_mask_len);
+  }
+  for (int x = lane; x < (n_pages + 31) / 32; x += 64) seen[x] = 0u;
+  __syncthreads();
+  const int32_t* row = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
+  for (int k = lane; k < len; k += 64) {
+    const int id = row[k];
+    if (id < 0 || id >= n_pages) { ++c_range; continue; }
+    if (id > i) ++c_causal;
+    const uint32_t bit = 1u << (id & 31);
+    if (atomicOr(&seen[id >> 5], bit) & bit) ++c_dup;
+    const int ph = a.page_table[(int64_t)s * a.max_pages + id];
+    if (ph < 0 || ph >= a.num_phys) ++c_phys;
+  }
+  // reduce over the wave, one atomic per counter
+  const int vals[5] = {c_range, c_causal, c_dup, c_len, c_phys};
+#pragma unroll
+  for (int c = 0; c < 5; ++c) {
+    int v = vals[c];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0 && v) atomicAdd(&a.bad[c], v);
+  }
+}
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, a.bad, 5);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.total_qblocks == 0) return err;
+  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)a.total_qblocks, (unsigned)a.hkv), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace cosa_osk

@@ -1,0 +1,67 @@
+// Launch interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cosa_osk {
+
+constexpr int kPage = 64;
+constexpr int kHeadDim = 128;
+constexpr int kMaxQBlocks = 16384;       // schedule keys live in LDS
+constexpr int kMaxMaskLen = 8191;        // schedule histogram lives in LDS
+constexpr int kMaxPagesPerSeq = 16384;   // visited-page bitmap lives in LDS
+constexpr int kMaxPagesBuilder = 8192;   // builder sort keys live in LDS
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* page_table;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_qblocks;
+  const int32_t* order_mask;
+  const int32_t* mask_len;
+  uint16_t* out;
+  float* lse;
+  uint8_t* decisions;
+  float* margins;
+  int32_t* sched;  // workspace: query-block visit order, [total_qblocks]
+  int64_t q_st, q_sh, o_st, o_sh, kv_sp, kv_sh, kv_st;
+  int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
+  float sm_scale;
+  float delta;
+};
+
+struct BuilderArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* page_table;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_qblocks;
+  int32_t* order_mask;
+  int32_t* mask_len;
+  float* scores;  // nullable
+  float* qbar;    // workspace [total_qblocks, hkv, 128]
+  float* kbar;    // workspace [total_qblocks, hkv, 128]
+  int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
+  int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
+  float budget1;
+  uint32_t flags;
+};
+
+struct ValidateArgs {
+  const int32_t* page_table;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_qblocks;
+  const int32_t* order_mask;
+  const int32_t* mask_len;
+  int32_t* bad;
+  int32_t num_seqs, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
+
+}  // namespace cosa_osk

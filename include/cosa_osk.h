@@ -1,0 +1,202 @@
+/*
+ * cosa_osk.h -- C ABI of the MI355X (gfx950) ordered-skipping block-sparse
+ * prefill attention library (libcosa_osk.so).
+ *
+ * What the library computes
+ * -------------------------
+ * Block-sparse causal prefill attention over a paged KV cache, as the CoSA
+ * paper ("Accelerating Long-Context Inference via Proxy-Kernel Co-Designed
+ * Sparse Attention") defines its Ordered-Skipping Kernel (OSK): section 4.3 and
+ * Appendix C, Algorithm A (attention loop).  Every 64-token query block i of a
+ * sequence visits the logical KV pages listed in its computation-order mask
+ * (section 4.2, Eq. (14): kept ids in visit order, -1 padding), in mask order,
+ * through the sequence's page table (physical page jumping and any-order page
+ * visiting, section 4.3).  It runs the tiled online softmax of section 3.1,
+ * Eq. (1)-(2), and skips the value side of a visited page in-kernel when the
+ * skip scale Delta > 0 and max_r(m_loc[r] - m[r]) < ln(Delta / N) (section 3.3,
+ * Eq. (5); Algorithm A line 14), N being the sequence's valid length, the max
+ * taken over the block's valid rows, and m updated before the test.  A query
+ * at causal position c attends to the tokens of its visited, non-skipped pages
+ * with t < L and t <= c (PageWeaver notes, section 2.1, Eq. (1)-(2)); an empty
+ * support gives a zero output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array pointers are DEVICE pointers owned by the caller.  The library
+ *   allocates and frees nothing; scratch space is the caller's workspace.
+ * - Calls are asynchronous on `stream` (0 = the null stream).  A negative status
+ *   is returned synchronously, before anything is launched, for a bad argument;
+ *   a launch failure is reported as COSA_ERR_HIP.
+ * - The library keeps no state between calls; calls are thread-safe.  Calls
+ *   that share a workspace must be ordered on one stream.
+ * - Supported: head_dim = 128, page_size = 64 (the query block equals the KV
+ *   page), bfloat16 Q/K/V/out, num_q_heads % num_kv_heads == 0.
+ *   Limits: total_qblocks <= 16384, max_mask_len <= 8191,
+ *   max_pages_per_seq <= 16384 (<= 8192 for the mask builder).  Anything else
+ *   returns COSA_ERR_UNSUPPORTED.
+ * - Layouts (element strides; head_dim is contiguous; strides are multiples of
+ *   8 elements and the base pointers are 16-byte aligned):
+ *     q, out        [total_q_tokens, num_q_heads, 128]   (sequences packed on T)
+ *     k_pool,v_pool [num_phys_pages, num_kv_heads, 64, 128] (same strides)
+ *     page_table    int32 [num_seqs, max_pages_per_seq]   logical -> physical page
+ *     cu_seqlens    int32 [num_seqs + 1]  token offsets; L_s = difference
+ *     cu_qblocks    int32 [num_seqs + 1]  prefix sums of ceil(L_s / 64)
+ *     order_mask    int32 [total_qblocks, num_kv_heads, max_mask_len]
+ *     mask_len      int32 [total_qblocks, num_kv_heads]
+ *   A query block's global index is qb = cu_qblocks[s] + i.  The q heads of a KV
+ *   head share its mask row (grouped-query heads share one page set per KV head,
+ *   PageWeaver notes section 2); skip votes are taken per q head.
+ */
+#ifndef COSA_OSK_H
+#define COSA_OSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COSA_ABI_VERSION 1
+
+typedef enum {
+  COSA_OK = 0,
+  COSA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad stride/alignment */
+  COSA_ERR_UNSUPPORTED = -2,  /* outside the supported shapes/limits listed above  */
+  COSA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required         */
+  COSA_ERR_HIP = -4           /* a HIP launch reported an error                      */
+} cosa_status_t;
+
+/* Decision-log codes (one byte per (query block, q head, mask position)). */
+#define COSA_DECISION_COMPUTED 0u    /* value side computed                          */
+#define COSA_DECISION_SKIPPED 1u     /* skipped in-kernel by Eq. (5)                 */
+#define COSA_DECISION_NOT_VISITED 2u /* padding, id outside [0, n_pages), id > i,
+                                        repeated id, or physical id outside the pool */
+
+/* Mask-builder flags: pages always kept. */
+#define COSA_FORCE_FIRST 1u  /* logical page 0 (attention sink)   */
+#define COSA_FORCE_DIAG 2u   /* the block's own (diagonal) page i */
+
+typedef struct cosa_osk_dims {
+  int32_t num_seqs;           /* >= 1 */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;           /* must be 128 */
+  int32_t page_size;          /* must be 64 */
+  int32_t total_q_tokens;     /* T = cu_seqlens[num_seqs] */
+  int32_t total_qblocks;      /* cu_qblocks[num_seqs] */
+  int32_t max_pages_per_seq;  /* row stride of page_table */
+  int32_t num_phys_pages;     /* pool size; a physical id outside [0, n) is not visited */
+  int32_t max_mask_len;       /* row stride of order_mask and of the decision log */
+  float sm_scale;             /* logit scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t reserved;           /* must be 0 */
+  int64_t q_stride_tok, q_stride_head;                  /* elements */
+  int64_t o_stride_tok, o_stride_head;                  /* elements */
+  int64_t kv_stride_page, kv_stride_head, kv_stride_tok; /* elements, K and V alike */
+} cosa_osk_dims_t;
+
+/* ABI version of the loaded library (COSA_ABI_VERSION it was built with). */
+int cosa_abi_version(void);
+
+/* Static, human-readable text of a status code. */
+const char* cosa_status_string(cosa_status_t status);
+
+/* Bytes of workspace cosa_osk_prefill needs for these dims (the unit schedule).
+ * Returns 0 if dims is NULL. Host-only. */
+size_t cosa_osk_workspace_bytes(const cosa_osk_dims_t* dims);
+
+/* Host-only validation of dims and the workspace size, the same checks
+ * cosa_osk_prefill runs before launching; touches no device. */
+cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_bytes);
+
+/*
+ * Ordered-skipping prefill attention (CoSA section 4.3; Appendix C, Algorithm A,
+ * attention loop; skip rule section 3.3, Eq. (5); per-query semantics PageWeaver
+ * notes section 2.1, Eq. (1)-(2)).
+ *
+ *   q, k_pool, v_pool  bfloat16 inputs (layouts above); read only.
+ *   page_table, cu_seqlens, cu_qblocks, order_mask, mask_len  int32; read only.
+ *       order_mask rows hold logical page ids in visit order; entries at
+ *       positions >= mask_len are ignored; inside the row, ids < 0, ids >=
+ *       ceil(L_s/64), ids > i and repeats of an earlier id are not visited
+ *       (cosa_validate_order_mask reports them).
+ *   budget2   the skip scale Delta of Eq. (5).  Delta <= 0 disables in-kernel
+ *             skipping (Delta = -1 is the pages' "off" value).  Otherwise the
+ *             threshold of sequence s is tau_s = ln(Delta / L_s) in natural-log
+ *             units of the scaled logits; a page is skipped iff the largest
+ *             (over the block's valid rows r) of m_loc[r] - m_new[r] is < tau_s.
+ *             Delta > L_s skips every page of that sequence (zero output).
+ *   out       bfloat16 [T, Hq, 128]; written for every valid token.
+ *   lse       nullable fp32 [T, Hq]: natural-log log-sum-exp of the scaled logits
+ *             over the computed keys (-inf where nothing was computed).
+ *   decisions nullable uint8 [total_qblocks, Hq, max_mask_len]: COSA_DECISION_*.
+ *   margins   nullable fp32, same shape: max_r(m_loc[r] - m_new[r]) in natural-
+ *             log units for visited positions, NaN elsewhere (requires decisions;
+ *             margins without decisions is COSA_ERR_INVALID_ARG).
+ *   workspace device scratch of >= cosa_osk_workspace_bytes(dims) bytes, 16-byte
+ *             aligned; its contents are overwritten.
+ * Numerics: fp32 accumulation of bf16 products for Q K^T, fp32 running max/sum,
+ * probabilities rounded to bf16 for the P V product, fp32 output accumulator,
+ * bf16 output.
+ */
+cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* cu_seqlens,
+                               const int32_t* cu_qblocks, const int32_t* order_mask,
+                               const int32_t* mask_len, float budget2,
+                               void* out, float* lse, uint8_t* decisions, float* margins,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Row width a computation-order mask built by cosa_build_order_mask needs:
+ * the longest |F_i| + ceil(budget1 * |R_i| - 1e-3) over blocks i < max_pages_per_seq
+ * (F_i: forced pages, R_i: the other causal pages).  Host-only.  Returns -1 for
+ * max_pages_per_seq < 1.
+ */
+int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t flags);
+
+/* Workspace bytes cosa_build_order_mask needs (pooled proxies). Host-only. */
+size_t cosa_build_order_mask_workspace_bytes(const cosa_osk_dims_t* dims);
+
+/*
+ * Computation-order mask from the mean-pooled q.k proxy (CoSA section 4.2,
+ * Eq. (14) for the mask format; the proxy is the dot product of mean-pooled
+ * query-block and key-page representations, kept pages visited in descending
+ * proxy order, as the paper's rewrite page describes it).  For every query
+ * block i of sequence s and KV head g:
+ *   qbar = sum over the group's q heads of the mean of q over the block's valid rows,
+ *   kbar_j = mean of k over the tokens t < L_s of logical page j,
+ *   score_j = qbar . kbar_j (fp32) for causal pages j <= i;
+ *   kept = forced pages (flags) + the top ceil(budget1 * |R_i| - 1e-3) of the
+ *   remaining causal pages R_i by (score descending, id ascending);
+ *   the row lists the kept ids in (score descending, id ascending) order, -1 after.
+ * order_mask [total_qblocks, Hkv, max_mask_len] and mask_len [total_qblocks, Hkv]
+ * are written; dims->max_mask_len must be >= cosa_order_mask_width(...).
+ * proxy_scores (nullable) fp32 [total_qblocks, Hkv, max_pages_per_seq]: score_j for
+ * j <= i, NaN after.  budget1 in [0, 1].  k_pool uses the dims' KV strides.
+ */
+cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                    const int32_t* page_table, const int32_t* cu_seqlens,
+                                    const int32_t* cu_qblocks, float budget1, uint32_t flags,
+                                    int32_t* order_mask, int32_t* mask_len, float* proxy_scores,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Count malformed mask entries (PageWeaver notes section 2.1 conventions: such
+ * entries add no interaction; the prefill treats them as not visited).
+ * bad_counts: device int32[5], zeroed by the call, then incremented:
+ *   [0] ids outside [0, ceil(L_s/64)) at positions < mask_len (includes -1),
+ *   [1] non-causal ids (j > i), [2] repeated ids in a row,
+ *   [3] mask_len outside [0, max_mask_len],
+ *   [4] referenced page-table entries outside [0, num_phys_pages).
+ */
+cosa_status_t cosa_validate_order_mask(const cosa_osk_dims_t* dims, const int32_t* page_table,
+                                       const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                                       const int32_t* order_mask, const int32_t* mask_len,
+                                       int32_t* bad_counts, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COSA_OSK_H */

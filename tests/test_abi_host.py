@@ -1,0 +1,112 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and its
+host-only argument checks return the documented status codes (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_long_osk_amd import binding
+from block_sparse_long_osk_amd.binding import CosaOskDims
+from oracle.maskref import FORCE_DIAG, FORCE_FIRST, mask_width
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(cosa_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(binding.EXPORTED) == names
+    assert binding.cosa_abi_version() == 1
+    assert binding.cosa_status_string(-3).startswith("workspace")
+
+
+def good_dims(**kw):
+    d = dict(num_seqs=1, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, total_q_tokens=4096,
+             total_qblocks=64, max_pages_per_seq=64, num_phys_pages=64, max_mask_len=20, sm_scale=0.0,
+             reserved=0, q_stride_tok=32 * 128, q_stride_head=128, o_stride_tok=32 * 128, o_stride_head=128,
+             kv_stride_page=8 * 64 * 128, kv_stride_head=64 * 128, kv_stride_tok=128)
+    d.update(kw)
+    return CosaOskDims(**d)
+
+
+def test_check_args_status_codes():
+    d = good_dims()
+    ws = binding.cosa_osk_workspace_bytes(d)
+    assert ws >= 64 * 4
+    assert binding.cosa_osk_check_args(d, ws) == OK
+    assert binding.cosa_osk_check_args(d, ws - 256) == WORKSPACE
+    assert binding.lib().cosa_osk_check_args(None, 1 << 20) == INVALID
+    cases = [
+        (dict(head_dim=64), UNSUPPORTED), (dict(page_size=128), UNSUPPORTED),
+        (dict(num_q_heads=30), UNSUPPORTED), (dict(max_mask_len=-1), INVALID),
+        (dict(max_mask_len=9000), UNSUPPORTED), (dict(total_qblocks=20000, total_q_tokens=20000 * 64), UNSUPPORTED),
+        (dict(max_pages_per_seq=20000), UNSUPPORTED), (dict(num_kv_heads=0), INVALID),
+        (dict(q_stride_head=100), INVALID), (dict(kv_stride_tok=0), INVALID),
+        (dict(total_q_tokens=64 * 64 + 1), INVALID), (dict(total_qblocks=65, total_q_tokens=64), INVALID),
+        (dict(reserved=1), INVALID), (dict(sm_scale=float("nan")), INVALID),
+    ]
+    for kw, want in cases:
+        dd = good_dims(**kw)
+        assert binding.cosa_osk_check_args(dd, 1 << 30) == want, kw
+
+
+def test_prefill_rejects_bad_arguments_before_launch():
+    """Null / misaligned pointers, missing workspace, margins without decisions and
+    a NaN skip scale are refused on the host (nothing is launched)."""
+    L = binding.lib()
+    d = good_dims()
+    ws = binding.cosa_osk_workspace_bytes(d)
+    fake = 0x10000  # never dereferenced: checks fail first
+    args = [fake] * 8
+    def call(q=fake, out=fake, dec=None, mar=None, work=fake, wsb=ws, budget=1.0, mask=fake):
+        return L.cosa_osk_prefill(ctypes.byref(d), q, fake, fake, fake, fake, fake, mask, fake, budget, out,
+                                  None, dec, mar, work, wsb, None)
+    assert call(q=None) == INVALID
+    assert call(out=fake + 2) == INVALID
+    assert call(mask=None) == INVALID
+    assert call(mar=fake) == INVALID
+    assert call(budget=float("nan")) == INVALID
+    assert call(work=None) == WORKSPACE
+    assert call(wsb=0) == WORKSPACE
+    assert L.cosa_osk_prefill(None, *([None] * 8), 1.0, None, None, None, None, None, 0, None) == INVALID
+
+
+@pytest.mark.parametrize("max_pages,b1,flags", [(32, 0.5, 3), (256, 0.25, 3), (512, 0.2, 3), (2048, 0.1, 3),
+                                                (100, 0.3, FORCE_FIRST), (77, 0.15, FORCE_DIAG), (5, 1.0, 0),
+                                                (1, 0.5, 3), (2, 0.0, 3)])
+def test_mask_width_matches_oracle(max_pages, b1, flags):
+    assert binding.cosa_order_mask_width(max_pages, b1, flags) == mask_width(max_pages, float(np.float32(b1)), flags)
+
+
+def test_builder_rejects_bad_arguments():
+    L = binding.lib()
+    d = good_dims(max_mask_len=5)
+    fake = 0x10000
+    need = binding.cosa_build_order_mask_workspace_bytes(d)
+    assert need >= 2 * 64 * 8 * 128 * 4
+    def call(dd=d, b1=0.1, flags=3, wsb=need, work=fake):
+        return L.cosa_build_order_mask(ctypes.byref(dd), fake, fake, fake, fake, fake, b1, flags, fake, fake,
+                                       None, work, wsb, None)
+    assert call(b1=1.5) == INVALID
+    assert call(flags=4) == INVALID
+    assert call(dd=good_dims(max_mask_len=3)) == INVALID          # narrower than the mask needs
+    assert call(dd=good_dims(max_mask_len=20), wsb=16) == WORKSPACE
+    assert call(dd=good_dims(max_mask_len=20, max_pages_per_seq=9000, total_qblocks=64)) == UNSUPPORTED
