@@ -58,13 +58,13 @@ def oracle_mask(batch, b1, flags=3):
 
 # --------------------------------------------------------------------------- small shapes
 def test_small_mha_random_masks_with_junk(rt):
-    wl = inputs.small_workload("mha300", [300], 1, 1, generator="structured", seed=11)
+    wl = inputs.small_workload("mha1000", [1000], 1, 1, generator="structured", seed=11)
     bt = inputs.generate(wl)
     rng = np.random.default_rng(5)
-    om, ml = random_masks(rng, [300], 1, 64, 9)
-    run_and_check(rt, "mha300/off", bt, om, ml, -1.0)
+    om, ml = random_masks(rng, [1000], 1, 64, 22, full_fraction=1.0)
+    run_and_check(rt, "mha1000/off", bt, om, ml, -1.0)
     d = delta_for_skip_fraction(bt, om, ml, 0.4)
-    st, _ = run_and_check(rt, "mha300/skip", bt, om, ml, d)
+    st, _ = run_and_check(rt, "mha1000/skip", bt, om, ml, d)
     assert st["skipped"] > 0
 
 
