@@ -1,0 +1,239 @@
+"""Benchmark of ordered-skipping block-sparse prefill attention on one MI355X.
+
+One step = one cosa_osk_prefill call over a whole layer (all 32 q heads, the
+128K-token sequence): the longest-first schedule kernel plus the ordered-
+skipping attention kernel.  Inputs (Q, the paged K/V pool, the page table and
+the computation-order mask built on the GPU by cosa_build_order_mask) are
+resident in HBM before the timed region.  Also timed: the same kernel with the
+dense causal mask and skipping off (the dense baseline), and the mask builder.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints one JSON line.  value = effective TFLOP/s on the visited blocks:
+QK^T flops of every visited (q head, page) plus P V flops of the computed ones,
+each 2*64*64*128, over the median call time.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TILE_FLOP = 2 * 64 * 64 * 128  # one 64x64x128 contraction
+KERNEL_SOURCES = ["block_sparse_long_osk_amd/csrc/osk_prefill.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "osk_prefill_cfg4_128k_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_calls(fn, steps, warmup):
+    """Per-call durations (ms) from HIP events on the current stream, plus the
+    wall time of the whole timed region bracketed by synchronizations."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in evs]
+    return per, wall
+
+
+def pct(xs, p):
+    xs = sorted(xs)
+    k = (len(xs) - 1) * p
+    lo, hi = math.floor(k), math.ceil(k)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def cpu_baseline(batch, wl, delta, budget_s=15.0):
+    """The fp64 oracle as it stands, timed on a bounded random sample of query
+    blocks (all KV heads of each), scaled to effective TFLOP/s."""
+    from block_sparse_long_osk_amd import inputs
+    from oracle import maskref, osk
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = 1
+    q = inputs.bf16_bits_to_f32(batch.q)
+    k = inputs.bf16_bits_to_f32(batch.k_pool)
+    v = inputs.bf16_bits_to_f32(batch.v_pool)
+    t_mask = time.perf_counter()
+    om, ml = maskref.build_order_mask(q, k, batch.page_table, batch.cu_seqlens, wl.num_kv_heads, wl.budget1)
+    t_mask = time.perf_counter() - t_mask
+    rng = np.random.default_rng(0)
+    order = rng.permutation(batch.total_qblocks)
+    flops = 0.0
+    spent = 0.0
+    n_blocks = 0
+    for qb in order:
+        units = [(int(qb), g) for g in range(wl.num_kv_heads)]
+        t = time.perf_counter()
+        res = osk.osk_reference(q, k, v, batch.page_table, batch.cu_seqlens, om, ml, delta, units=units)
+        spent += time.perf_counter() - t
+        d = res["decisions"][qb]
+        flops += TILE_FLOP * (float((d != 2).sum()) + float((d == 0).sum()))
+        n_blocks += 1
+        if spent >= budget_s:
+            break
+    rate = flops / spent / 1e12
+    return {"value": rate, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{n_blocks} random query blocks x {wl.num_kv_heads} KV heads of {wl.name} "
+                      f"(mask rows from the CPU reference builder, {t_mask:.1f} s, not timed)",
+            "seconds": round(spent, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--workload", default="cfg4_128k_structured")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
+                    help="counters: a plain 1 GiB device copy (the counter scale reference), then "
+                         "--steps OSK calls; for rocprofv3 --pmc passes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the kernel shards by KV head or by "
+              "query-block range without exchange inside a layer, but multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_osk_amd import binding, inputs, runner
+    binding.lib()
+    wl = inputs.WORKLOADS[args.workload]
+    delta = inputs.skip_scale(args.workload)
+    print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
+    batch = inputs.generate(wl)
+    db = runner.upload(batch)
+    torch.cuda.synchronize()
+
+    # ---- computation-order mask on the GPU (timed separately)
+    om, ml = runner.build_mask(db, wl.budget1)
+    if args.mode == "counters":
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                                                  # plain copy: reads and writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        for _ in range(args.steps):
+            runner.prefill(db, om, ml, delta)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "counters", "workload": wl.name, "copy_bytes": 1 << 30,
+                          "osk_calls": args.steps, "kernel_source_hash": kernel_source_hash()}))
+        return
+    width = om.shape[2]
+    ws_b = torch.empty(binding.cosa_build_order_mask_workspace_bytes(db.dims(width)), dtype=torch.uint8,
+                       device="cuda")
+    builder_ms, _ = time_calls(lambda: runner.build_mask(db, wl.budget1, workspace=ws_b), 5, 2)
+
+    # ---- one logged (untimed) call: visited / computed counts for the flop count
+    logged = runner.prefill(db, om, ml, delta, log=True)
+    torch.cuda.synchronize()
+    dec = logged.decisions
+    visited = int((dec != 2).sum().item())
+    computed = int((dec == 0).sum().item())
+    del logged, dec
+    flop = TILE_FLOP * (visited + computed)
+
+    # ---- timed OSK calls (no logging)
+    outs = runner.allocate_outputs(db, width, log=False)
+    outs.lse = None
+    ws = runner.workspace_for(db, width)
+    step = lambda: runner.prefill(db, om, ml, delta, outputs=outs, workspace=ws)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    per, wall = time_calls(step, args.steps, args.warmup)
+    med = statistics.median(per)
+    ms_per_step = wall / args.steps
+    tflops = flop / (med * 1e-3) / 1e12
+
+    # ---- dense-mask baseline: same kernel, every causal page, skipping off
+    dense = None
+    if not args.no_dense:
+        dom, dml = runner.dense_mask(db)
+        d_visited = int(dml.sum().item()) * (db.num_q_heads // db.num_kv_heads)
+        d_flop = 2 * TILE_FLOP * d_visited
+        douts = runner.allocate_outputs(db, dom.shape[2], log=False)
+        douts.lse = None
+        dws = runner.workspace_for(db, dom.shape[2])
+        print(f"[bench] timing dense baseline", file=sys.stderr, flush=True)
+        dper, _ = time_calls(lambda: runner.prefill(db, dom, dml, -1.0, outputs=douts, workspace=dws),
+                             args.dense_steps, 1)
+        dmed = statistics.median(dper)
+        dense = {"ms_per_layer": dmed, "tflops": d_flop / (dmed * 1e-3) / 1e12,
+                 "frac_of_peak": d_flop / (dmed * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "visited_q_head_pages": d_visited, "algorithmic_tflop": d_flop / 1e12}
+        del douts, dom, dml
+
+    # ---- roofline of the dominant kernel
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("workload") == wl.name and tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    kv_bytes = 2 * 64 * 128 * 2 * (visited // (db.num_q_heads // db.num_kv_heads))
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "osk_prefill_kernel<4> (+ schedule kernel, <0.1% of the call)",
+                "algorithmic_flop_per_launch": flop,
+                "kv_gather_gbs": kv_bytes / (med * 1e-3) / 1e9,
+                "kv_gather_frac_of_hbm": kv_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+    cpu = None
+    if not args.no_cpu:
+        print(f"[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(batch, wl, delta)
+        cpu["ms_per_layer_extrapolated"] = flop / (cpu["value"] * 1e12) * 1e3
+
+    n_q_visits = visited
+    rec = {
+        "metric": "OSK prefill ms/layer + effective TFLOP/s at 128K; speedup vs dense-mask",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "ms_per_layer_median": med, "ms_p10": pct(per, 0.1), "ms_p90": pct(per, 0.9),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded structured generator; no dataset or model weights)",
+        "config": {"workload": wl.name, "seq_len": wl.seq_lens[0] if len(wl.seq_lens) == 1 else list(wl.seq_lens),
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": 128,
+                   "page_size": 64, "budget1": wl.budget1, "skip_scale_delta": delta},
+        "visited_q_head_pages": n_q_visits, "computed_q_head_pages": computed,
+        "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
+        "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
+        "dense": dense, "mask_builder_ms": statistics.median(builder_ms),
+        "osk_plus_builder_ms": med + statistics.median(builder_ms),
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,6 +28,9 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms stay off in all device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in VGPRs: the softmax reads S with plain VALU ops and AGPRs
+           # serve as spill space instead of holding S and O behind copy instructions
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     cmd += ["-o", tmp]

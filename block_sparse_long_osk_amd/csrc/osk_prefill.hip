@@ -50,6 +50,7 @@ constexpr int kTileBytes = kPage * kHeadDim * 2;  // one K or V page of one KV h
 constexpr int kWindow = 512;                      // mask entries resolved per window
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
+constexpr float kRebase = 8.f;  // log2 headroom of the lazily moved exponent base
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -261,8 +262,12 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
     }
   }
 
-  // ---- online-softmax state (log2 domain, scaled): running max m2, row sum l2, O^T accumulators
+  // ---- online-softmax state (log2 domain, scaled).  m2: the running row max of Eq. (2),
+  //      which the skip vote uses.  b2: the exponent base of l2 and O; it follows m2 lazily
+  //      (moved only when m2 exceeds it by more than kRebase, so p = 2^(s - b2) <= 2^kRebase)
+  //      -- O / l is unchanged by the choice of base, and the rescale of O becomes rare.
   float m2[2] = {-INFINITY, -INFINITY};
+  float b2[2] = {-INFINITY, -INFINITY};
   float l2[2] = {0.f, 0.f};
   f32x16_t o[4][2];
 #pragma unroll
@@ -333,14 +338,14 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
 
     if (nv > 0) {
       {
-        const int64_t off = (int64_t)vis_phys[0] * a.kv_sp + kv_head_off;
+        const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[0]) * a.kv_sp + kv_head_off;
         issue_page_loads<W>(a.k + off, a.v + off, a.kv_st, lds + buf * kTileBytes,
                             lds + (2 + buf) * kTileBytes, wave, lane);
       }
       for (int v = 0; v < nv; ++v) {
         wait_vmem_all();
         __syncthreads();  // page v resident; every wave is done with the other buffer
-        const int j = vis_j[v];
+        const int j = __builtin_amdgcn_readfirstlane(vis_j[v]);
         LDS_PTR(uint8_t) kb = lds + buf * kTileBytes;
         LDS_PTR(uint8_t) vb = lds + (2 + buf) * kTileBytes;
         const int tail_rows = min(kPage, L - j * kPage);  // valid tokens on page j
@@ -352,7 +357,7 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
           __syncthreads();
         }
         if (v + 1 < nv) {
-          const int64_t off = (int64_t)vis_phys[v + 1] * a.kv_sp + kv_head_off;
+          const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[v + 1]) * a.kv_sp + kv_head_off;
           issue_page_loads<W>(a.k + off, a.v + off, a.kv_st, lds + (buf ^ 1) * kTileBytes,
                               lds + (2 + (buf ^ 1)) * kTileBytes, wave, lane);
         }
@@ -410,18 +415,30 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
           dec_lds[wave][vis_k[v] - k0] = skip ? 1 : 0;
           mar_lds[wave][vis_k[v] - k0] = margin2 * kLn2;
         }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          alpha[rt] = (mnew2[rt] == -INFINITY) ? 1.f : exp2f(m2[rt] - mnew2[rt]);
-          m2[rt] = mnew2[rt];
-        }
+        m2[0] = mnew2[0];
+        m2[1] = mnew2[1];
         if (!skip) {
-          // ---- P = exp(S - m) as bf16 B operands; row sums; rescale; O^T += V^T P^T
+          // ---- move the exponent base if some row's max passed it by more than kRebase
+          if (__ballot(m2[0] > b2[0] + kRebase || m2[1] > b2[1] + kRebase)) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              alpha[rt] = (m2[rt] == -INFINITY) ? 1.f : exp2f(b2[rt] - m2[rt]);
+              b2[rt] = m2[rt];
+              l2[rt] *= alpha[rt];
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[nt][rt][e] *= alpha[rt];
+          }
+          // ---- P = 2^(S' - b) as bf16 B operands; row sums; O^T += V^T P^T
           bf16x8_t pb[2][4];
           float rs[2] = {0.f, 0.f};
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt) {
-            const float msub = (mnew2[rt] == -INFINITY) ? 0.f : mnew2[rt];
+            const float msub = (b2[rt] == -INFINITY) ? 0.f : b2[rt];
 #pragma unroll
             for (int tc = 0; tc < 4; ++tc) {
               bf16x8_t pv;
@@ -435,15 +452,7 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
             }
           }
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) l2[rt] = alpha[rt] * l2[rt] + permlane32_sum(rs[rt]);
-          if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-              for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[nt][rt][e] *= alpha[rt];
-          }
+          for (int rt = 0; rt < 2; ++rt) l2[rt] += permlane32_sum(rs[rt]);
 #pragma unroll
           for (int tc = 0; tc < 4; ++tc) {
 #pragma unroll
@@ -504,7 +513,7 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
     }
     if (a.lse != nullptr && hi == 0 && row_ok[rt]) {
       a.lse[(int64_t)(tok0 + i * kPage + r) * a.hq + h] =
-          l2[rt] > 0.f ? (m2[rt] + log2f(l2[rt])) * kLn2 : -INFINITY;
+          l2[rt] > 0.f ? (b2[rt] + log2f(l2[rt])) * kLn2 : -INFINITY;
     }
   }
 }
