@@ -422,7 +422,7 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
           if (__ballot(m2[0] > b2[0] + kRebase || m2[1] > b2[1] + kRebase)) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-              alpha[rt] = (m2[rt] == -INFINITY) ? 1.f : exp2f(b2[rt] - m2[rt]);
+              alpha[rt] = (m2[rt] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(b2[rt] - m2[rt]);
               b2[rt] = m2[rt];
               l2[rt] *= alpha[rt];
             }
@@ -444,7 +444,7 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
               bf16x8_t pv;
 #pragma unroll
               for (int kk = 0; kk < 8; ++kk) {
-                const float p = exp2f(fmaf(acc[tc >> 1][rt][8 * (tc & 1) + kk], scale_log2, -msub));
+                const float p = __builtin_amdgcn_exp2f(fmaf(acc[tc >> 1][rt][8 * (tc & 1) + kk], scale_log2, -msub));
                 rs[rt] += p;
                 pv[kk] = (__bf16)p;
               }
