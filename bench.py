@@ -174,6 +174,9 @@ def main():
     per, wall = time_calls(step, args.steps, args.warmup)
     med = statistics.median(per)
     ms_per_step = wall / args.steps
+    aborts = runner.abort_count(db, ws, width)
+    if aborts:
+        print(f"[bench] {aborts} workgroups reported aborted inter-wave waits", file=sys.stderr)
     tflops = flop / (med * 1e-3) / 1e12
 
     # ---- dense-mask baseline: same kernel, every causal page, skipping off
@@ -230,7 +233,7 @@ def main():
         "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
         "dense": dense, "mask_builder_ms": statistics.median(builder_ms),
         "osk_plus_builder_ms": med + statistics.median(builder_ms),
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "aborted_workgroups": aborts,
     }
     print(json.dumps(rec), flush=True)
 

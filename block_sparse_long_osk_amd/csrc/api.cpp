@@ -67,9 +67,14 @@ const char* cosa_status_string(cosa_status_t status) {
   return "unknown status";
 }
 
+// workspace layout: [schedule: total_qblocks int32, padded to 256 B][status: 256 B]
+static size_t schedule_bytes(const cosa_osk_dims_t* dims) {
+  return round_up((size_t)dims->total_qblocks * sizeof(int32_t) + 1);
+}
+
 size_t cosa_osk_workspace_bytes(const cosa_osk_dims_t* dims) {
   if (dims == nullptr || dims->total_qblocks < 0) return 0;
-  return round_up((size_t)dims->total_qblocks * sizeof(int32_t) + 1);
+  return schedule_bytes(dims) + kAlign;
 }
 
 cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_bytes) {
@@ -108,6 +113,7 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   a.decisions = decisions;
   a.margins = margins;
   a.sched = static_cast<int32_t*>(workspace);
+  a.error_count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + schedule_bytes(dims));
   a.q_st = dims->q_stride_tok;
   a.q_sh = dims->q_stride_head;
   a.o_st = dims->o_stride_tok;

@@ -9,27 +9,31 @@
 // PageWeaver notes, section 2.1, Eq. (1): t < L and t <= c.
 //
 // Organisation on the chip:
-// * one workgroup = one (query block, KV head[, head subgroup]) unit, W waves,
-//   one wave per q head of the KV head's group: the W heads share every K/V
-//   page tile staged in LDS (grouped-query packing) and vote independently;
-// * a wave owns its q head's 64 query rows; it computes S^T = K Q^T with
-//   v_mfma_f32_32x32x16_bf16 so that each lane holds one query row (lane%32)
-//   and half of that row's 64 logits: the row max and row sum need one
-//   permlane32 swap, the 64-row skip vote one 32-lane butterfly;
-// * O^T = V^T P^T: the probabilities go from the S^T accumulators straight
-//   into the B operand (bf16) with no data movement; V^T comes from the
-//   row-major V tile through ds_read_b64_tr_b16 (transposing LDS read);
-// * K and V page tiles are gathered with global_load_lds_dwordx4 (direct to
-//   LDS, no VGPR staging) into a double buffer: the page of visit v+1 is in
-//   flight while visit v computes; XOR swizzles keep LDS reads conflict-free;
+// * one workgroup = one (query block, KV head[, head subgroup]) unit with HW q
+//   heads of the KV head's group; two waves per head, each owning 32 of the
+//   block's 64 query rows (2*HW waves, two waves per SIMD at HW = 4, so one
+//   wave's softmax VALU work runs under another wave's MFMAs).  The two halves
+//   of a head combine their partial vote margins through LDS: one vote per
+//   (q head, 64-row block);
+// * a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so each lane holds
+//   one query row (lane%32) and half of that row's 64 logits: row max and row
+//   sum need one permlane32 swap, the 32-row partial vote one DPP reduction;
+// * O^T = V^T P^T: the probabilities go from the S^T accumulators straight into
+//   the B operand (bf16); V^T comes from the row-major V tile through
+//   ds_read_b64_tr_b16 (transposing LDS read);
+// * K and V page tiles are gathered with global_load_lds_dwordx4 (direct to LDS,
+//   no VGPR staging) into a ring of kRing page slots; every wave gathers its
+//   share of each page kRing-1 visits ahead.  LDS counters say when a slot's
+//   page has landed (ready) and when every wave is done with it (used), so the
+//   heads of a group are not held in lock step by a per-visit barrier: a head
+//   that skips a page runs ahead of one that computes it;
 // * the visit list of a unit (mask row -> validity -> page table -> physical
-//   page, first occurrence of a repeated id only) is resolved in LDS windows
-//   of 512 entries before the visits, so the hot loop does no dependent
-//   global index loads;
-// * a one-workgroup schedule kernel orders query blocks by mask length
-//   (longest first; stable), and the grid walks that order with the KV head
-//   minor, so consecutive workgroups (which the dispatcher spreads over the 8
-//   XCDs round-robin) put each KV head's pages on its own XCD's L2.
+//   page, first occurrence of a repeated id only) is resolved in LDS windows of
+//   512 entries before the visits, so the hot loop does no dependent global loads;
+// * a one-workgroup schedule kernel orders query blocks by mask length (longest
+//   first; stable), and the grid walks that order with the KV head minor, so
+//   consecutive workgroups (which the dispatcher spreads over the 8 XCDs round-
+//   robin) keep each KV head's pages in one XCD's L2.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -42,12 +46,15 @@ namespace cosa_osk {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(8))) short s16x8_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
-typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 constexpr int kTileBytes = kPage * kHeadDim * 2;  // one K or V page of one KV head: 16 KiB
+constexpr int kPageBytes = 2 * kTileBytes;        // K then V
 constexpr int kWindow = 512;                      // mask entries resolved per window
+constexpr int kRing = 4;                          // page slots in flight per workgroup
+constexpr int kSpinLimit = 1 << 22;               // bound of every inter-wave wait
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kRebase = 8.f;  // log2 headroom of the lazily moved exponent base
@@ -68,20 +75,66 @@ __device__ __forceinline__ uint32_t permlane32_partner(uint32_t x, int lane) {
   auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return lane < 32 ? r[1] : r[0];
 }
-// max over the 32 lanes of each wave half (both halves hold the same rows)
-__device__ __forceinline__ float half_wave_max(float x) {
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-__device__ __forceinline__ float uniform_f(float x) {
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+// max over lanes 0..31 (lanes 32..63 hold the same rows), returned wave-uniform
+__device__ __forceinline__ float max_lanes32(float x) {
+  const int ninf = __float_as_int(-INFINITY);
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x111, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x112, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x114, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), 0x118, 0xF, 0xF, false)));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The page gathers are issued from inline assembly: the compiler does not see
+// them as LDS writes, so it does not wait for them before unrelated LDS reads;
+// their completion is tracked explicitly with vmcnt (the visit loop issues no
+// other vector-memory instruction).
+__device__ __forceinline__ void dma_16B(const void* gsrc, uint32_t lds_byte_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds_byte_addr)
+      : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// wait until at most `pages` pages' worth of this wave's gather instructions are outstanding
+template <int PW>
+__device__ __forceinline__ void wait_pages_outstanding(int pages) {
+  if (pages <= 0) wait_vmcnt<0>();
+  else if (pages == 1) wait_vmcnt<PW>();
+  else if (pages == 2) wait_vmcnt<2 * PW>();
+  else wait_vmcnt<3 * PW>();
+}
+
+__device__ __forceinline__ int lds_load_acquire(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_add_release(int* p, int v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Bounded wait until *ctr >= target.  Every wave of the workgroup is resident,
+// and each counter is advanced by waves that never wait on a later visit, so
+// the wait ends; the bound turns a broken protocol into an abort, never a hang.
+__device__ __forceinline__ bool wait_at_least(int* ctr, int target, int* abort_flag) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (__builtin_amdgcn_readfirstlane(lds_load_acquire(ctr)) >= target) return true;
+    if (__builtin_amdgcn_readfirstlane(lds_load_acquire(abort_flag)) != 0) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __hip_atomic_store(abort_flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return false;
+}
 
 // XOR swizzle of the 16-byte granule index inside a 256-byte K row (t = key row):
 // the 32 lanes of an MFMA A-operand read hit 16 distinct granules per 16 rows.
@@ -90,21 +143,26 @@ __device__ __forceinline__ int swz_k(int t, int granule) { return granule ^ (t &
 // four rows each ds_read_b64_tr_b16 lane group touches fall in distinct banks.
 __device__ __forceinline__ int swz_v(int t, int granule) { return granule ^ (2 * ((0x6530 >> (4 * (t & 3))) & 0xF)); }
 
-// Gather one page's K and V tile (64 tokens x 128 dims of one KV head) into
-// LDS with direct-to-LDS 16-byte loads.  Granule p of the tile lands at LDS
-// byte 16*p; it holds token t = p/16 and the (swizzled) source granule.
-template <int W>
-__device__ __forceinline__ void issue_page_loads(const uint16_t* kpage, const uint16_t* vpage, int64_t kv_st,
-                                                 LDS_PTR(uint8_t) kdst, LDS_PTR(uint8_t) vdst, int wave, int lane) {
+// This wave's share (PW of the page's 32 one-KiB blocks: 16 of K, 16 of V) of
+// one page's gather into the ring slot at LDS byte address slot_addr.  Granule
+// p of a tile lands at byte 16*p and holds token t = p/16; on the tail page,
+// tokens at or past the valid count read row 0 instead (their logits are masked;
+// their values then stay finite, so a zero probability never meets a non-finite
+// value).
+template <int NW, int PW>
+__device__ __forceinline__ void gather_page_share(const uint16_t* kpage, const uint16_t* vpage, int64_t kv_st,
+                                                  uint32_t slot_addr, int valid_rows, int wave, int lane) {
 #pragma unroll
-  for (int x = 0; x < 16 / W; ++x) {
-    const int m = x * W + wave;
-    const int p = m * 64 + lane;
+  for (int x = 0; x < PW; ++x) {
+    const int m = x * NW + wave;  // block 0..31
+    const int blk = m & 15;
+    const int p = blk * 64 + lane;
     const int t = p >> 4, gs = p & 15;
-    const uint16_t* ks = kpage + t * kv_st + swz_k(t, gs) * 8;
-    const uint16_t* vs = vpage + t * kv_st + swz_v(t, gs) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)ks, (LDS_PTR(void))(kdst + m * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)vs, (LDS_PTR(void))(vdst + m * 1024), 16, 0, 0);
+    const int ts = t < valid_rows ? t : 0;
+    const uint16_t* src = (m < 16) ? kpage + ts * kv_st + swz_k(t, gs) * 8 : vpage + ts * kv_st + swz_v(t, gs) * 8;
+    // the LDS base goes to M0 and must be wave-uniform (it is: m depends on the wave only)
+    dma_16B(src, __builtin_amdgcn_readfirstlane(slot_addr + (m < 16 ? 0u : (uint32_t)kTileBytes) +
+                                                (uint32_t)blk * 1024u));
   }
 }
 
@@ -121,7 +179,6 @@ __device__ __forceinline__ bf16x8_t read_vt(LDS_PTR(const uint8_t) vb, int nt, i
   const int off1 = t1 * 256 + swz_v(t1, n >> 3) * 16 + (n & 7) * 2;
   s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(vb + off0));
   s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(vb + off1));
-  typedef __attribute__((ext_vector_type(8))) short s16x8_t;
   s16x8_t c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8_t, c);
 }
@@ -130,12 +187,14 @@ __device__ __forceinline__ bf16x8_t read_vt(LDS_PTR(const uint8_t) vb, int nt, i
 // schedule: query blocks ordered by mask length, longest first (stable)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void osk_schedule_kernel(const int32_t* __restrict__ mask_len, int n_qb, int hkv,
-                                                             int max_len, int32_t* __restrict__ order) {
+                                                             int max_len, int32_t* __restrict__ order,
+                                                             int32_t* __restrict__ error_count) {
   __shared__ uint16_t key[kMaxQBlocks];
   __shared__ int hist[kMaxMaskLen + 1];
   __shared__ int partial[1024];
   const int tid = threadIdx.x;
   const int nbins = max_len + 1;
+  if (tid == 0) *error_count = 0;
   for (int b = tid; b < nbins; b += 1024) hist[b] = 0;
   __syncthreads();
   for (int qb = tid; qb < n_qb; qb += 1024) {
@@ -200,24 +259,32 @@ __global__ __launch_bounds__(1024) void osk_schedule_kernel(const int32_t* __res
 // ---------------------------------------------------------------------------
 // the ordered-skipping prefill kernel
 // ---------------------------------------------------------------------------
-template <int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[4 * kTileBytes];  // K0 K1 V0 V1
+template <int HW>
+__global__ __launch_bounds__(128 * HW) void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
+  constexpr int NW = 2 * HW;   // waves
+  constexpr int NT = 64 * NW;  // threads
+  constexpr int PW = 32 / NW;  // page-gather instructions per wave per page
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
   __shared__ int raw_id[kWindow];
   __shared__ int raw_phys[kWindow];
   __shared__ int vis_phys[kWindow];
   __shared__ int vis_j[kWindow];
   __shared__ int vis_k[kWindow];
   __shared__ uint32_t seen_bits[kMaxPagesPerSeq / 32];
+  __shared__ uint8_t dec_lds[HW][kWindow];
+  __shared__ float mar_lds[HW][kWindow];
+  __shared__ int ready_ctr[kRing];
+  __shared__ int used_ctr[kRing];
+  __shared__ int vote_seq[HW][2][2];
+  __shared__ float vote_val[HW][2][2];
   __shared__ int s_count;
-  __shared__ uint8_t dec_lds[W][kWindow];
-  __shared__ float mar_lds[W][kWindow];
+  __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int hi = lane >> 5;
-  const int nthreads = 64 * W;
+  const int half = wave & 1;  // rows 32*half .. +31 of the block; the halves of a head sit on different SIMDs
+  const int hl = wave >> 1;   // head within the workgroup
 
   // ---- which unit: schedule position (block order), KV head (minor), head subgroup
   const int per_qb = a.hkv * nsub;
@@ -226,7 +293,7 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
   const int g = rem / nsub;
   const int sub = rem - g * nsub;
   const int qb = a.sched[pos];
-  const int h = g * heads_per_group + sub * W + wave;
+  const int h = g * heads_per_group + sub * HW + hl;
   int lo = 0, hi_s = a.num_seqs;
   while (hi_s - lo > 1) {
     const int mid = (lo + hi_s) >> 1;
@@ -243,22 +310,21 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
   const float scale_log2 = a.sm_scale * kLog2e;
   const float tau2 = skip_on ? (float)(log2((double)a.delta) - log2((double)L)) : 0.f;
   const bool logging = a.decisions != nullptr;
-  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))kv_lds;
+  LDS_PTR(uint8_t) ring_lds = (LDS_PTR(uint8_t))ring;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring_lds;
 
-  // ---- this wave's 64 query rows as MFMA B operands: lane holds row 32 rt + lane%32,
+  // ---- this wave's 32 query rows as MFMA B operands: lane holds row 32*half + lane%32,
   //      dims 16 c + 8 hi .. +8
-  bf16x8_t qf[2][8];
-  bool row_ok[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = rt * 32 + (lane & 31);
-    row_ok[rt] = (i * kPage + r) < L;
-    const uint16_t* qrow = a.q + (int64_t)(tok0 + i * kPage + r) * a.q_st + (int64_t)h * a.q_sh + hi * 8;
+  const int r_blk = half * 32 + (lane & 31);
+  const bool row_ok = (i * kPage + r_blk) < L;
+  bf16x8_t qf[8];
+  {
+    const uint16_t* qrow = a.q + (int64_t)(tok0 + i * kPage + r_blk) * a.q_st + (int64_t)h * a.q_sh + hi * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       i32x4_t x = {0, 0, 0, 0};
-      if (row_ok[rt]) x = *(const i32x4_t*)(qrow + c * 16);
-      qf[rt][c] = __builtin_bit_cast(bf16x8_t, x);
+      if (row_ok) x = *(const i32x4_t*)(qrow + c * 16);
+      qf[c] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
 
@@ -266,29 +332,26 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
   //      which the skip vote uses.  b2: the exponent base of l2 and O; it follows m2 lazily
   //      (moved only when m2 exceeds it by more than kRebase, so p = 2^(s - b2) <= 2^kRebase)
   //      -- O / l is unchanged by the choice of base, and the rescale of O becomes rare.
-  float m2[2] = {-INFINITY, -INFINITY};
-  float b2[2] = {-INFINITY, -INFINITY};
-  float l2[2] = {0.f, 0.f};
-  f32x16_t o[4][2];
+  float m2 = -INFINITY, b2 = -INFINITY, l2 = 0.f;
+  f32x16_t o[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[nt][rt][e] = 0.f;
+    for (int e = 0; e < 16; ++e) o[nt][e] = 0.f;
 
-  for (int x = threadIdx.x; x < (n_pages + 31) / 32; x += nthreads) seen_bits[x] = 0u;
+  for (int x = threadIdx.x; x < (n_pages + 31) / 32; x += NT) seen_bits[x] = 0u;
+  if (threadIdx.x == 0) s_abort = 0;
 
   const int len = min(max(a.mask_len[(int64_t)qb * a.hkv + g], 0), a.max_mask_len);
   const int32_t* mrow = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
   const int32_t* pt_row = a.page_table + (int64_t)s * a.max_pages;
-  const int64_t kv_head_off = (int64_t)g * a.kv_sh;
-  int buf = 0;
+  const uint16_t* kbase = a.k + (int64_t)g * a.kv_sh;
+  const uint16_t* vbase = a.v + (int64_t)g * a.kv_sh;
 
   for (int k0 = 0; k0 < len; k0 += kWindow) {
     const int wl = min(kWindow, len - k0);
     // (A) resolve the window's entries in parallel: validity and page table
-    for (int e = threadIdx.x; e < wl; e += nthreads) {
+    for (int e = threadIdx.x; e < wl; e += NT) {
       const int id = mrow[k0 + e];
       int ph = -1;
       if (id >= 0 && id < n_pages && id <= i) {
@@ -298,8 +361,10 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
       raw_id[e] = ph >= 0 ? id : -1;
       raw_phys[e] = ph;
     }
-    if (logging)
-      for (int x = lane; x < wl; x += 64) { dec_lds[wave][x] = 2; mar_lds[wave][x] = __builtin_nanf(""); }
+    if (logging && half == 0)
+      for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
+    if (threadIdx.x < kRing) { ready_ctr[threadIdx.x] = 0; used_ctr[threadIdx.x] = 0; }
+    if (threadIdx.x < 4 * HW) (&vote_seq[0][0][0])[threadIdx.x] = 0;
     __syncthreads();
     // (B) wave 0 compacts the visited entries in mask order; a repeated id keeps
     //     only its first occurrence (bitmap over the sequence's pages)
@@ -336,147 +401,150 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
     __syncthreads();
     const int nv = s_count;
 
-    if (nv > 0) {
-      {
-        const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[0]) * a.kv_sp + kv_head_off;
-        issue_page_loads<W>(a.k + off, a.v + off, a.kv_st, lds + buf * kTileBytes,
-                            lds + (2 + buf) * kTileBytes, wave, lane);
-      }
-      for (int v = 0; v < nv; ++v) {
-        wait_vmem_all();
-        __syncthreads();  // page v resident; every wave is done with the other buffer
-        const int j = __builtin_amdgcn_readfirstlane(vis_j[v]);
-        LDS_PTR(uint8_t) kb = lds + buf * kTileBytes;
-        LDS_PTR(uint8_t) vb = lds + (2 + buf) * kTileBytes;
-        const int tail_rows = min(kPage, L - j * kPage);  // valid tokens on page j
-        if (tail_rows < kPage) {
-          // tokens past L on the tail page: zero their V rows (their logits are masked,
-          // and a zero probability must not meet a non-finite value)
-          for (int x = threadIdx.x; x < (kPage - tail_rows) * 16; x += nthreads)
-            *(LDS_PTR(i32x4_t))(vb + tail_rows * 256 + x * 16) = i32x4_t{0, 0, 0, 0};
-          __syncthreads();
-        }
-        if (v + 1 < nv) {
-          const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[v + 1]) * a.kv_sp + kv_head_off;
-          issue_page_loads<W>(a.k + off, a.v + off, a.kv_st, lds + (buf ^ 1) * kTileBytes,
-                              lds + (2 + (buf ^ 1)) * kTileBytes, wave, lane);
-        }
+    // ---- ring prologue: gather pages 0 .. kRing-2, announce 0 .. kRing-3
+    const int pro = min(kRing - 1, nv);
+    for (int p = 0; p < pro; ++p) {
+      const int jp = __builtin_amdgcn_readfirstlane(vis_j[p]);
+      const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[p]) * a.kv_sp;
+      gather_page_share<NW, PW>(kbase + off, vbase + off, a.kv_st, ring_addr + (uint32_t)(p % kRing) * kPageBytes,
+                                min(kPage, L - jp * kPage), wave, lane);
+    }
+    for (int p = 0; p < min(kRing - 2, nv); ++p) {
+      wait_pages_outstanding<PW>(pro - 1 - p);
+      if (lane == 0) lds_add_release(&ready_ctr[p % kRing], 1);
+    }
 
-        // ---- S^T = K Q^T for 64 keys x 64 query rows (fp32 accumulate)
-        f32x16_t acc[2][2];
+    for (int v = 0; v < nv; ++v) {
+      const int slot = v % kRing;
+      // ---- keep kRing-1 pages in flight: gather page v+kRing-1 once every wave is done
+      //      with the page that held its slot, then announce page v+kRing-2
+      const int u = v + kRing - 1;
+      const int issued = min(u, nv - 1);
+      if (u < nv) {
+        if (!wait_at_least(&used_ctr[u % kRing], NW * (u / kRing), &s_abort)) break;
+        const int ju = __builtin_amdgcn_readfirstlane(vis_j[u]);
+        const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[u]) * a.kv_sp;
+        gather_page_share<NW, PW>(kbase + off, vbase + off, a.kv_st, ring_addr + (uint32_t)(u % kRing) * kPageBytes,
+                                  min(kPage, L - ju * kPage), wave, lane);
+      }
+      const int sgn = v + kRing - 2;
+      if (sgn < nv) {
+        wait_pages_outstanding<PW>(issued - sgn);
+        if (lane == 0) lds_add_release(&ready_ctr[sgn % kRing], 1);
+      }
+      // ---- page v resident in its slot (every wave's share has landed)
+      if (!wait_at_least(&ready_ctr[slot], NW * (v / kRing + 1), &s_abort)) break;
+      const int j = __builtin_amdgcn_readfirstlane(vis_j[v]);
+      LDS_PTR(const uint8_t) kb = ring_lds + slot * kPageBytes;
+      LDS_PTR(const uint8_t) vb = kb + kTileBytes;
+      const int tail_rows = min(kPage, L - j * kPage);  // valid tokens on page j
+
+      // ---- S^T = K Q^T for 64 keys x 32 query rows (fp32 accumulate)
+      f32x16_t acc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[tt][e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = tt * 32 + (lane & 31);
+          const bf16x8_t ka = *(LDS_PTR(const bf16x8_t))(kb + t * 256 + swz_k(t, 2 * c + hi) * 16);
+          acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], acc[tt], 0, 0, 0);
+        }
+      }
+      // ---- visibility on the diagonal and tail pages: t <= c and t < L
+      if (j == i || tail_rows < kPage) {
+        const int c_tok = i * kPage + r_blk;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[tt][rt][e] = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int t = tt * 32 + (lane & 31);
-            const bf16x8_t ka = *(LDS_PTR(const bf16x8_t))(kb + t * 256 + swz_k(t, 2 * c + hi) * 16);
-            acc[tt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][c], acc[tt][0], 0, 0, 0);
-            acc[tt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][c], acc[tt][1], 0, 0, 0);
+          for (int e = 0; e < 16; ++e) {
+            const int t = j * kPage + tt * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if (t > c_tok || t >= L) acc[tt][e] = -INFINITY;
           }
-        }
-        // ---- visibility on the diagonal and tail pages: t <= c and t < L
-        if (j == i || tail_rows < kPage) {
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                const int t = j * kPage + tt * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-                const int c = i * kPage + rt * 32 + (lane & 31);
-                if (t > c || t >= L) acc[tt][rt][e] = -INFINITY;
-              }
-        }
-        // ---- local row max, running-max update, block vote (Eq. (1), (2), (5))
-        float mnew2[2], alpha[2];
-        float dmax = -INFINITY;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[tt][rt][e]);
-          mx = permlane32_max(mx);
-          const float mloc2 = mx * scale_log2;
-          mnew2[rt] = fmaxf(m2[rt], mloc2);
-          const float dd = (row_ok[rt] && mloc2 != -INFINITY) ? (mloc2 - mnew2[rt]) : -INFINITY;
-          dmax = fmaxf(dmax, dd);
-        }
-        const float margin2 = uniform_f(half_wave_max(dmax));
-        const bool skip = skip_on && (margin2 < tau2);
-        if (logging && lane == 0) {
-          dec_lds[wave][vis_k[v] - k0] = skip ? 1 : 0;
-          mar_lds[wave][vis_k[v] - k0] = margin2 * kLn2;
-        }
-        m2[0] = mnew2[0];
-        m2[1] = mnew2[1];
-        if (!skip) {
-          // ---- move the exponent base if some row's max passed it by more than kRebase
-          if (__ballot(m2[0] > b2[0] + kRebase || m2[1] > b2[1] + kRebase)) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-              alpha[rt] = (m2[rt] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(b2[rt] - m2[rt]);
-              b2[rt] = m2[rt];
-              l2[rt] *= alpha[rt];
-            }
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-              for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[nt][rt][e] *= alpha[rt];
-          }
-          // ---- P = 2^(S' - b) as bf16 B operands; row sums; O^T += V^T P^T
-          bf16x8_t pb[2][4];
-          float rs[2] = {0.f, 0.f};
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const float msub = (b2[rt] == -INFINITY) ? 0.f : b2[rt];
-#pragma unroll
-            for (int tc = 0; tc < 4; ++tc) {
-              bf16x8_t pv;
-#pragma unroll
-              for (int kk = 0; kk < 8; ++kk) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(acc[tc >> 1][rt][8 * (tc & 1) + kk], scale_log2, -msub));
-                rs[rt] += p;
-                pv[kk] = (__bf16)p;
-              }
-              pb[rt][tc] = pv;
-            }
-          }
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) l2[rt] += permlane32_sum(rs[rt]);
-#pragma unroll
-          for (int tc = 0; tc < 4; ++tc) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-              const bf16x8_t va = read_vt(vb, nt, tc, lane);
-              o[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[0][tc], o[nt][0], 0, 0, 0);
-              o[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[1][tc], o[nt][1], 0, 0, 0);
-            }
-          }
-        }
-        buf ^= 1;
       }
+      // ---- local row max, running-max update, block vote (Eq. (1), (2), (5))
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[tt][e]);
+      mx = permlane32_max(mx);
+      const float mloc2 = mx * scale_log2;
+      const float mnew2 = fmaxf(m2, mloc2);
+      const float dd = (row_ok && mloc2 != -INFINITY) ? (mloc2 - mnew2) : -INFINITY;
+      const float my_margin = max_lanes32(dd);
+      // exchange the 32-row partial margin with the other half of this head
+      const int par = v & 1;
+      if (lane == 0) {
+        vote_val[hl][half][par] = my_margin;
+        __hip_atomic_store(&vote_seq[hl][half][par], v + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (!wait_at_least(&vote_seq[hl][half ^ 1][par], v + 1, &s_abort)) break;
+      const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(
+                                                  __float_as_int(vote_val[hl][half ^ 1][par]))));
+      const bool skip = skip_on && (margin2 < tau2);
+      if (logging && half == 0 && lane == 0) {
+        dec_lds[hl][vis_k[v] - k0] = skip ? 1 : 0;
+        mar_lds[hl][vis_k[v] - k0] = margin2 * kLn2;
+      }
+      m2 = mnew2;
+      if (!skip) {
+        // ---- move the exponent base if some row's max passed it by more than kRebase
+        if (__ballot(m2 > b2 + kRebase)) {
+          const float alpha = (m2 == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(b2 - m2);
+          b2 = m2;
+          l2 *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[nt][e] *= alpha;
+        }
+        // ---- P = 2^(S' - b) as bf16 B operands; row sums; O^T += V^T P^T
+        const float msub = (b2 == -INFINITY) ? 0.f : b2;
+        bf16x8_t pb[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int tc = 0; tc < 4; ++tc) {
+          bf16x8_t pv;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(acc[tc >> 1][8 * (tc & 1) + kk], scale_log2, -msub));
+            rs += p;
+            pv[kk] = (__bf16)p;
+          }
+          pb[tc] = pv;
+        }
+        l2 += permlane32_sum(rs);
+#pragma unroll
+        for (int tc = 0; tc < 4; ++tc) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const bf16x8_t va = read_vt(vb, nt, tc, lane);
+            o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tc], o[nt], 0, 0, 0);
+          }
+        }
+      }
+      // every LDS read of this slot has returned (the release waits for the wave's
+      // outstanding LDS reads before the count moves)
+      if (lane == 0) lds_add_release(&used_ctr[slot], 1);
     }
-    if (logging) {
+    wait_vmcnt<0>();  // no page gather may still be writing LDS past this point
+    __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
+    if (logging && half == 0) {
       uint8_t* drow = a.decisions + ((int64_t)qb * a.hq + h) * a.max_mask_len + k0;
       float* mrw = a.margins ? a.margins + ((int64_t)qb * a.hq + h) * a.max_mask_len + k0 : nullptr;
       for (int x = lane; x < wl; x += 64) {
-        drow[x] = dec_lds[wave][x];
-        if (mrw) mrw[x] = mar_lds[wave][x];
+        drow[x] = dec_lds[hl][x];
+        if (mrw) mrw[x] = mar_lds[hl][x];
       }
     }
-    __syncthreads();  // window LDS (visit list, log) is reused by the next window
+    if (s_abort != 0) break;
+    __syncthreads();
   }
-  if (logging) {
+  if (logging && half == 0) {
     uint8_t* drow = a.decisions + ((int64_t)qb * a.hq + h) * a.max_mask_len;
     float* mrw = a.margins ? a.margins + ((int64_t)qb * a.hq + h) * a.max_mask_len : nullptr;
     for (int x = len + lane; x < a.max_mask_len; x += 64) {
@@ -484,56 +552,49 @@ void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
       if (mrw) mrw[x] = __builtin_nanf("");
     }
   }
+  if (threadIdx.x == 0 && s_abort != 0) atomicAdd(a.error_count, 1);
 
   // ---- epilogue: O <- O / l (0 when nothing was computed), bf16 out, natural-log LSE
-  float inv_l[2];
+  const float inv_l = l2 > 0.f ? 1.f / l2 : 0.f;
+  uint16_t* orow = a.out + (int64_t)(tok0 + i * kPage + r_blk) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) inv_l[rt] = l2[rt] > 0.f ? 1.f / l2[rt] : 0.f;
+  for (int nt = 0; nt < 4; ++nt) {
+    const f32x16_t ov = o[nt] * inv_l;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = rt * 32 + (lane & 31);
-    uint16_t* orow = a.out + (int64_t)(tok0 + i * kPage + r) * a.o_st + (int64_t)h * a.o_sh;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        // lane (hi=0) holds dims 32nt+16mm+{0..3, 8..11}; its partner (hi=1) {4..7, 12..15}
-        const f32x16_t ov = o[nt][rt] * inv_l[rt];
-        const uint32_t r0a = pack_bf16x2(ov[8 * mm + 0], ov[8 * mm + 1]);
-        const uint32_t r0b = pack_bf16x2(ov[8 * mm + 2], ov[8 * mm + 3]);
-        const uint32_t r1a = pack_bf16x2(ov[8 * mm + 4], ov[8 * mm + 5]);
-        const uint32_t r1b = pack_bf16x2(ov[8 * mm + 6], ov[8 * mm + 7]);
-        const uint32_t sa = hi ? r0a : r1a, sb = hi ? r0b : r1b;
-        const uint32_t ra = permlane32_partner(sa, lane), rb = permlane32_partner(sb, lane);
-        i32x4_t st;
-        if (hi == 0) st = i32x4_t{(int)r0a, (int)r0b, (int)ra, (int)rb};
-        else st = i32x4_t{(int)ra, (int)rb, (int)r1a, (int)r1b};
-        if (row_ok[rt]) *(i32x4_t*)(orow + nt * 32 + mm * 16 + hi * 8) = st;
-      }
-    }
-    if (a.lse != nullptr && hi == 0 && row_ok[rt]) {
-      a.lse[(int64_t)(tok0 + i * kPage + r) * a.hq + h] =
-          l2[rt] > 0.f ? (b2[rt] + log2f(l2[rt])) * kLn2 : -INFINITY;
+    for (int mm = 0; mm < 2; ++mm) {
+      // lane (hi=0) holds dims 32nt+16mm+{0..3, 8..11}; its partner (hi=1) {4..7, 12..15}
+      const uint32_t r0a = pack_bf16x2(ov[8 * mm + 0], ov[8 * mm + 1]);
+      const uint32_t r0b = pack_bf16x2(ov[8 * mm + 2], ov[8 * mm + 3]);
+      const uint32_t r1a = pack_bf16x2(ov[8 * mm + 4], ov[8 * mm + 5]);
+      const uint32_t r1b = pack_bf16x2(ov[8 * mm + 6], ov[8 * mm + 7]);
+      const uint32_t sa = hi ? r0a : r1a, sb = hi ? r0b : r1b;
+      const uint32_t ra = permlane32_partner(sa, lane), rb = permlane32_partner(sb, lane);
+      i32x4_t st;
+      if (hi == 0) st = i32x4_t{(int)r0a, (int)r0b, (int)ra, (int)rb};
+      else st = i32x4_t{(int)ra, (int)rb, (int)r1a, (int)r1b};
+      if (row_ok) *(i32x4_t*)(orow + nt * 32 + mm * 16 + hi * 8) = st;
     }
   }
+  if (a.lse != nullptr && hi == 0 && row_ok)
+    a.lse[(int64_t)(tok0 + i * kPage + r_blk) * a.hq + h] = l2 > 0.f ? (b2 + log2f(l2)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.total_qblocks == 0) return hipSuccess;
   const int G = a.hq / a.hkv;
-  const int W = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int nsub = G / W;
+  const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const int nsub = G / HW;
   hipLaunchKernelGGL(osk_schedule_kernel, dim3(1), dim3(1024), 0, stream, a.mask_len, a.total_qblocks, a.hkv,
-                     a.max_mask_len, a.sched);
+                     a.max_mask_len, a.sched, a.error_count);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)a.total_qblocks * (unsigned)a.hkv * (unsigned)nsub);
-  if (W == 4)
-    hipLaunchKernelGGL(osk_prefill_kernel<4>, grid, dim3(256), 0, stream, a, G, nsub);
-  else if (W == 2)
-    hipLaunchKernelGGL(osk_prefill_kernel<2>, grid, dim3(128), 0, stream, a, G, nsub);
+  if (HW == 4)
+    hipLaunchKernelGGL(osk_prefill_kernel<4>, grid, dim3(512), 0, stream, a, G, nsub);
+  else if (HW == 2)
+    hipLaunchKernelGGL(osk_prefill_kernel<2>, grid, dim3(256), 0, stream, a, G, nsub);
   else
-    hipLaunchKernelGGL(osk_prefill_kernel<1>, grid, dim3(64), 0, stream, a, G, nsub);
+    hipLaunchKernelGGL(osk_prefill_kernel<1>, grid, dim3(128), 0, stream, a, G, nsub);
   return hipGetLastError();
 }
 

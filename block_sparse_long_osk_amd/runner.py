@@ -84,6 +84,13 @@ def workspace_for(db: DeviceBatch, max_mask_len: int):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=db.q.device)
 
 
+def abort_count(db: DeviceBatch, workspace, max_mask_len: int) -> int:
+    """The workspace's health word after a completed call (0 when healthy)."""
+    import torch
+    n = binding.cosa_osk_workspace_bytes(db.dims(max_mask_len))
+    return int(workspace[n - 256:n - 252].view(torch.int32).item())
+
+
 def prefill(db: DeviceBatch, order_mask, mask_len, delta: float, log: bool = False,
             outputs: Optional[PrefillOutputs] = None, workspace=None, stream=None,
             sm_scale: float = 0.0) -> PrefillOutputs:

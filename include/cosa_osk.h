@@ -135,7 +135,10 @@ cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_
  *             log units for visited positions, NaN elsewhere (requires decisions;
  *             margins without decisions is COSA_ERR_INVALID_ARG).
  *   workspace device scratch of >= cosa_osk_workspace_bytes(dims) bytes, 16-byte
- *             aligned; its contents are overwritten.
+ *             aligned; its contents are overwritten.  After the call completes, the
+ *             int32 at byte offset cosa_osk_workspace_bytes(dims) - 256 holds the
+ *             number of workgroups whose bounded inter-wave waits gave up (0 in every
+ *             healthy run; nonzero means the output of those blocks is not valid).
  * Numerics: fp32 accumulation of bf16 products for Q K^T, fp32 running max/sum,
  * probabilities rounded to bf16 for the P V product, fp32 output accumulator,
  * bf16 output.

@@ -42,8 +42,10 @@ def run_and_check(rt, name, batch, om, ml, delta, units=None):
         "mask", om.shape, "delta", delta)
     db = rt.upload(batch)
     omd, mld = rt.upload_mask(om, ml)
-    outs = rt.prefill(db, omd, mld, delta, log=True)
+    ws = rt.workspace_for(db, om.shape[2])
+    outs = rt.prefill(db, omd, mld, delta, log=True, workspace=ws)
     torch.cuda.synchronize()
+    assert rt.abort_count(db, ws, om.shape[2]) == 0, "inter-wave waits aborted"
     gpu = gpu_to_host(outs)
     stats = check_prefill(batch, om, ml, delta, gpu, units)
     log(name, stats)
