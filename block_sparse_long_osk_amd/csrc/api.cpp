@@ -37,6 +37,8 @@ cosa_status_t check_dims(const cosa_osk_dims_t* d) {
       !stride_ok(d->kv_stride_tok))
     return COSA_ERR_INVALID_ARG;
   if (isnan(d->sm_scale) || isinf(d->sm_scale)) return COSA_ERR_INVALID_ARG;
+  // page gathers address a page's tokens with 32-bit byte offsets
+  if (d->kv_stride_tok > (int64_t)1 << 24) return COSA_ERR_UNSUPPORTED;
   return COSA_OK;
 }
 

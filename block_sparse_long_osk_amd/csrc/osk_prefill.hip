@@ -94,19 +94,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // The page gathers are issued from inline assembly: the compiler does not see
 // them as LDS writes, so it does not wait for them before unrelated LDS reads;
 // their completion is tracked explicitly with vmcnt (the visit loop issues no
-// other vector-memory instruction).
-__device__ __forceinline__ void dma_16B(const void* gsrc, uint32_t lds_byte_addr) {
+// other vector-memory instruction).  One 16-byte granule per lane, from a
+// wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane byte offset, to LDS
+// byte address lds_byte_addr + 16 * lane.
+__device__ __forceinline__ void dma_16B_saddr(const void* sbase, uint32_t voff, uint32_t lds_byte_addr) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(gsrc), "s"(lds_byte_addr)
+      : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
       : "memory", "m0");
 }
+// vmcnt holds at most 63; waiting for fewer outstanding instructions is always safe
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N > 63 ? 63 : N) : "memory");
 }
 // wait until at most `pages` pages' worth of this wave's gather instructions are outstanding
 template <int PW>
@@ -143,42 +146,91 @@ __device__ __forceinline__ int swz_k(int t, int granule) { return granule ^ (t &
 // four rows each ds_read_b64_tr_b16 lane group touches fall in distinct banks.
 __device__ __forceinline__ int swz_v(int t, int granule) { return granule ^ (2 * ((0x6530 >> (4 * (t & 3))) & 0xF)); }
 
-// This wave's share (PW of the page's 32 one-KiB blocks: 16 of K, 16 of V) of
-// one page's gather into the ring slot at LDS byte address slot_addr.  Granule
-// p of a tile lands at byte 16*p and holds token t = p/16; on the tail page,
-// tokens at or past the valid count read row 0 instead (their logits are masked;
-// their values then stay finite, so a zero probability never meets a non-finite
-// value).
-template <int NW, int PW>
-__device__ __forceinline__ void gather_page_share(const uint16_t* kpage, const uint16_t* vpage, int64_t kv_st,
-                                                  uint32_t slot_addr, int valid_rows, int wave, int lane) {
-#pragma unroll
-  for (int x = 0; x < PW; ++x) {
-    const int m = x * NW + wave;  // block 0..31
-    const int blk = m & 15;
-    const int p = blk * 64 + lane;
-    const int t = p >> 4, gs = p & 15;
-    const int ts = t < valid_rows ? t : 0;
-    const uint16_t* src = (m < 16) ? kpage + ts * kv_st + swz_k(t, gs) * 8 : vpage + ts * kv_st + swz_v(t, gs) * 8;
-    // the LDS base goes to M0 and must be wave-uniform (it is: m depends on the wave only)
-    dma_16B(src, __builtin_amdgcn_readfirstlane(slot_addr + (m < 16 ? 0u : (uint32_t)kTileBytes) +
-                                                (uint32_t)blk * 1024u));
-  }
+// Hides a value from the optimiser (empty asm), e.g. to keep a cheap per-lane term
+// from being hoisted out of a loop into a long-lived register.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
-// A operand of O^T = V^T P^T for n-tile nt (32 output dims) and key chunk tc
-// (16 keys): lane l holds V[t][n] for n = 32 nt + l%32 and the 8 keys
-// t = 16 tc + 8 (kk/4) + 4 (l/32) + kk%4, kk = 0..7 -- the same key order in
-// which the lane's S^T accumulator entries feed the B operand.
-__device__ __forceinline__ bf16x8_t read_vt(LDS_PTR(const uint8_t) vb, int nt, int tc, int lane) {
+// Gather of K and V page tiles into LDS.  A tile is 16 one-KiB blocks; with NW
+// waves, wave w issues blocks b = x*NW + w (x < 16/NW), and lane l of block b
+// fills row 4b + l/16, granule l%16 (the granule order of the swizzles above).
+// The swizzle terms depend on the row only through its low 4 (K) or 2 (V) bits,
+// so a per-lane byte offset (row within the block + swizzled granule) serves
+// every block of the wave -- two for K when NW = 2, where odd blocks are 8 rows
+// off -- and the block's row base goes into the scalar address.  On a tail page
+// (fewer than 64 valid tokens) rows at or past the valid count read row 0: their
+// logits are masked and their values stay finite, so a zero probability never
+// meets a non-finite value.
+template <int NW>
+struct TileGather {
+  static constexpr int kBlocks = 16 / NW;  // blocks per wave per tile
+  uint32_t lane_k[2], lane_v;
+  int kv_st;  // token stride in elements (the host bounds it so offsets fit in 32 bits)
+
+  __device__ __forceinline__ void init(int64_t kv_stride_tok, int wave, int lane) {
+    kv_st = (int)kv_stride_tok;
+    const int trow = lane >> 4;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      lane_k[x] = (uint32_t)(trow * kv_st + swz_k(4 * (x * NW + wave) + trow, lane & 15) * 8) * 2u;
+    lane_v = (uint32_t)(trow * kv_st + swz_v(trow, lane & 15) * 8) * 2u;
+  }
+  // this wave's share of one tile (valid_rows rows hold data) into the slot at LDS byte address slot
+  __device__ __forceinline__ void issue(const uint16_t* tile, uint32_t slot, int valid_rows, bool is_v, int wave,
+                                        int lane) const {
+    if (valid_rows >= kPage) {
+#pragma unroll
+      for (int x = 0; x < kBlocks; ++x) {
+        const int b = x * NW + wave;
+        dma_16B_saddr(tile + 4 * b * kv_st, is_v ? lane_v : lane_k[x & 1], slot + (uint32_t)b * 1024u);
+      }
+    } else {
+      // rare: the lane terms are recomputed here rather than kept in registers
+      const int ln = (int)opaque((uint32_t)lane);
+#pragma unroll
+      for (int x = 0; x < kBlocks; ++x) {
+        const int b = x * NW + wave;
+        const int t = 4 * b + (ln >> 4);
+        const int ts = t < valid_rows ? t : 0;
+        const uint32_t voff = (uint32_t)(ts * kv_st + (is_v ? swz_v(t, ln & 15) : swz_k(t, ln & 15)) * 8) * 2u;
+        dma_16B_saddr(tile, voff, slot + (uint32_t)b * 1024u);
+      }
+    }
+  }
+};
+
+
+// LDS operand addressing.  The swizzles above only touch address bits 4..7, so an
+// operand address is a per-lane base XOR a per-chunk constant, plus an immediate
+// offset.  The per-lane base of a tile is formed once per tile and hidden from the
+// optimiser (empty asm), so that the chunk addresses are not hoisted out of the
+// visit loop into a dozen loop-invariant registers.
+template <class T>
+__device__ __forceinline__ LDS_PTR(const T) lds_at(uint32_t byte_addr) {
+  return (LDS_PTR(const T))(uintptr_t)byte_addr;
+}
+// K tile: A operand of S^T = K Q^T for key tile tt (32 keys) and dim chunk c
+// (16 dims): lane l reads key t = 32 tt + l%32, dims 16 c + 8 (l/32) .. +8, at
+// t*256 + swz_k(t, 2c + l/32)*16 = (base ^ (c << 5)) + 8192 tt.
+__device__ __forceinline__ uint32_t k_lane_base(uint32_t kb, int lane) {
+  return opaque(kb + (uint32_t)((lane & 31) * 256 + (((lane >> 5) ^ (lane & 15)) << 4)));
+}
+// V tile: A operand of O^T = V^T P^T for n-tile nt (32 output dims) and key chunk
+// tc (16 keys): lane l holds V[t][n] for n = 32 nt + l%32 and the 8 keys
+// t = 16 tc + 8 (kk/4) + 4 (l/32) + kk%4, kk = 0..7 -- the same key order in which
+// the lane's S^T accumulator entries feed the B operand.  Two ds_read_b64_tr_b16
+// (keys kk < 4 and kk >= 4, 8 rows apart) at (base ^ (nt << 6)) + 4096 tc (+2048).
+__device__ __forceinline__ uint32_t v_lane_base(uint32_t vb, int lane) {
   const int hi = lane >> 5, nhalf = (lane >> 4) & 1, e = (lane & 15) >> 2, qq = lane & 3;
-  const int n = nt * 32 + nhalf * 16 + qq * 4;
-  const int t0 = tc * 16 + hi * 4 + e;
-  const int t1 = t0 + 8;
-  const int off0 = t0 * 256 + swz_v(t0, n >> 3) * 16 + (n & 7) * 2;
-  const int off1 = t1 * 256 + swz_v(t1, n >> 3) * 16 + (n & 7) * 2;
-  s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(vb + off0));
-  s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))(vb + off1));
+  const int sw = 2 * ((0x6530 >> (4 * e)) & 0xF);  // swz_v's row term for rows t = e mod 4
+  return opaque(vb + (uint32_t)((hi * 4 + e) * 256 + (((2 * nhalf + (qq >> 1)) ^ sw) << 4) + (qq & 1) * 8));
+}
+__device__ __forceinline__ bf16x8_t read_vt(uint32_t vbase_lane, int nt, int tc) {
+  const uint32_t a0 = (vbase_lane ^ (uint32_t)(nt << 6)) + (uint32_t)tc * 4096u;
+  s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))lds_at<s16x4_t>(a0));
+  s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4_t))lds_at<s16x4_t>(a0 + 2048u));
   s16x8_t c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8_t, c);
 }
@@ -257,306 +309,265 @@ __global__ __launch_bounds__(1024) void osk_schedule_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// the ordered-skipping prefill kernel
+// pieces shared by the two prefill kernels
 // ---------------------------------------------------------------------------
+// One workgroup's unit: a query block (by schedule position), a KV head, and the
+// HW q heads hl = 0..HW-1 of subgroup `sub` of that KV head's group.
+struct Unit {
+  int qb, g, h, i, tok0, L, n_pages, len;
+  const int32_t* pt_row;
+};
+
 template <int HW>
-__global__ __launch_bounds__(128 * HW) void osk_prefill_kernel(const PrefillArgs a, int heads_per_group, int nsub) {
-  constexpr int NW = 2 * HW;   // waves
-  constexpr int NT = 64 * NW;  // threads
-  constexpr int PW = 32 / NW;  // page-gather instructions per wave per page
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
-  __shared__ int raw_id[kWindow];
-  __shared__ int raw_phys[kWindow];
-  __shared__ int vis_phys[kWindow];
-  __shared__ int vis_j[kWindow];
-  __shared__ int vis_k[kWindow];
-  __shared__ uint32_t seen_bits[kMaxPagesPerSeq / 32];
-  __shared__ uint8_t dec_lds[HW][kWindow];
-  __shared__ float mar_lds[HW][kWindow];
-  __shared__ int ready_ctr[kRing];
-  __shared__ int used_ctr[kRing];
-  __shared__ int vote_seq[HW][2][2];
-  __shared__ float vote_val[HW][2][2];
-  __shared__ int s_count;
-  __shared__ int s_abort;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hi = lane >> 5;
-  const int half = wave & 1;  // rows 32*half .. +31 of the block; the halves of a head sit on different SIMDs
-  const int hl = wave >> 1;   // head within the workgroup
-
-  // ---- which unit: schedule position (block order), KV head (minor), head subgroup
+__device__ __forceinline__ Unit decode_unit(const PrefillArgs& a, int heads_per_group, int nsub, int hl) {
+  Unit u;
   const int per_qb = a.hkv * nsub;
   const int pos = blockIdx.x / per_qb;
   const int rem = blockIdx.x - pos * per_qb;
-  const int g = rem / nsub;
-  const int sub = rem - g * nsub;
-  const int qb = a.sched[pos];
-  const int h = g * heads_per_group + sub * HW + hl;
+  u.g = rem / nsub;
+  const int sub = rem - u.g * nsub;
+  u.qb = a.sched[pos];
+  u.h = u.g * heads_per_group + sub * HW + hl;
   int lo = 0, hi_s = a.num_seqs;
   while (hi_s - lo > 1) {
     const int mid = (lo + hi_s) >> 1;
-    if (a.cu_qblocks[mid] <= qb) lo = mid; else hi_s = mid;
+    if (a.cu_qblocks[mid] <= u.qb) lo = mid; else hi_s = mid;
   }
-  const int s = lo;
-  const int i = qb - a.cu_qblocks[s];
-  const int tok0 = a.cu_seqlens[s];
-  const int L = a.cu_seqlens[s + 1] - tok0;
+  u.i = u.qb - a.cu_qblocks[lo];
+  u.tok0 = a.cu_seqlens[lo];
+  u.L = a.cu_seqlens[lo + 1] - u.tok0;
   // pages addressable through the page table (cu_seqlens and max_pages_per_seq agree
   // for well-formed inputs; the clamp keeps every table and bitmap access in bounds)
-  const int n_pages = min((L + kPage - 1) / kPage, a.max_pages);
-  const bool skip_on = a.delta > 0.f;
-  const float scale_log2 = a.sm_scale * kLog2e;
-  const float tau2 = skip_on ? (float)(log2((double)a.delta) - log2((double)L)) : 0.f;
-  const bool logging = a.decisions != nullptr;
-  LDS_PTR(uint8_t) ring_lds = (LDS_PTR(uint8_t))ring;
-  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring_lds;
+  u.n_pages = min((u.L + kPage - 1) / kPage, a.max_pages);
+  u.len = min(max(a.mask_len[(int64_t)u.qb * a.hkv + u.g], 0), a.max_mask_len);
+  u.pt_row = a.page_table + (int64_t)lo * a.max_pages;
+  return u;
+}
 
-  // ---- this wave's 32 query rows as MFMA B operands: lane holds row 32*half + lane%32,
-  //      dims 16 c + 8 hi .. +8
-  const int r_blk = half * 32 + (lane & 31);
-  const bool row_ok = (i * kPage + r_blk) < L;
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qrow = a.q + (int64_t)(tok0 + i * kPage + r_blk) * a.q_st + (int64_t)h * a.q_sh + hi * 8;
+// The wave's 32 query rows as MFMA B operands: lane holds row r_blk, dims
+// 16 c + 8 hi .. +8 (zero for rows past the sequence end).
+__device__ __forceinline__ void load_q(const PrefillArgs& a, const Unit& u, int r_blk, bool row_ok, int hi,
+                                       bf16x8_t (&qf)[8]) {
+  const uint16_t* qrow = a.q + (int64_t)(u.tok0 + u.i * kPage + r_blk) * a.q_st + (int64_t)u.h * a.q_sh + hi * 8;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      i32x4_t x = {0, 0, 0, 0};
-      if (row_ok) x = *(const i32x4_t*)(qrow + c * 16);
-      qf[c] = __builtin_bit_cast(bf16x8_t, x);
-    }
+  for (int c = 0; c < 8; ++c) {
+    i32x4_t x = {0, 0, 0, 0};
+    if (row_ok) x = *(const i32x4_t*)(qrow + c * 16);
+    qf[c] = __builtin_bit_cast(bf16x8_t, x);
   }
+  // Q must have landed before the visit loop: otherwise the compiler places its
+  // vmcnt wait inside the loop, where it would also drain the in-flight page gathers
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
+}
 
-  // ---- online-softmax state (log2 domain, scaled).  m2: the running row max of Eq. (2),
-  //      which the skip vote uses.  b2: the exponent base of l2 and O; it follows m2 lazily
-  //      (moved only when m2 exceeds it by more than kRebase, so p = 2^(s - b2) <= 2^kRebase)
-  //      -- O / l is unchanged by the choice of base, and the rescale of O becomes rare.
-  float m2 = -INFINITY, b2 = -INFINITY, l2 = 0.f;
-  f32x16_t o[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[nt][e] = 0.f;
+// Visit list of one window of the mask row, in LDS.
+struct WindowLds {
+  int raw_id[kWindow];
+  int raw_phys[kWindow];
+  int vis_phys[kWindow];
+  int vis_j[kWindow];
+  int vis_k[kWindow];
+  uint32_t seen_bits[kMaxPagesPerSeq / 32];
+  int count;
+};
 
-  for (int x = threadIdx.x; x < (n_pages + 31) / 32; x += NT) seen_bits[x] = 0u;
-  if (threadIdx.x == 0) s_abort = 0;
-
-  const int len = min(max(a.mask_len[(int64_t)qb * a.hkv + g], 0), a.max_mask_len);
-  const int32_t* mrow = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
-  const int32_t* pt_row = a.page_table + (int64_t)s * a.max_pages;
-  const uint16_t* kbase = a.k + (int64_t)g * a.kv_sh;
-  const uint16_t* vbase = a.v + (int64_t)g * a.kv_sh;
-
-  for (int k0 = 0; k0 < len; k0 += kWindow) {
-    const int wl = min(kWindow, len - k0);
-    // (A) resolve the window's entries in parallel: validity and page table
-    for (int e = threadIdx.x; e < wl; e += NT) {
-      const int id = mrow[k0 + e];
-      int ph = -1;
-      if (id >= 0 && id < n_pages && id <= i) {
-        ph = pt_row[id];
-        if (ph < 0 || ph >= a.num_phys) ph = -1;
-      }
-      raw_id[e] = ph >= 0 ? id : -1;
-      raw_phys[e] = ph;
+// Resolve mask entries k0 .. k0+wl-1 into the window's visit list: an entry is
+// visited when its id is a causal page of the sequence (0 <= id <= i, id below the
+// page count) with a valid physical page, and only at its first occurrence in the
+// row (bitmap over the sequence's pages, kept across windows).  Returns the number
+// of visits.  Called by every thread of the workgroup; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& u, const int32_t* mrow, int k0,
+                                              int wl, WindowLds& w, int wave, int lane) {
+  for (int e = threadIdx.x; e < wl; e += NT) {
+    const int id = mrow[k0 + e];
+    int ph = -1;
+    if (id >= 0 && id < u.n_pages && id <= u.i) {
+      ph = u.pt_row[id];
+      if (ph < 0 || ph >= a.num_phys) ph = -1;
     }
-    if (logging && half == 0)
-      for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
-    if (threadIdx.x < kRing) { ready_ctr[threadIdx.x] = 0; used_ctr[threadIdx.x] = 0; }
-    if (threadIdx.x < 4 * HW) (&vote_seq[0][0][0])[threadIdx.x] = 0;
-    __syncthreads();
-    // (B) wave 0 compacts the visited entries in mask order; a repeated id keeps
-    //     only its first occurrence (bitmap over the sequence's pages)
-    if (wave == 0) {
-      int count = 0;
-      for (int c0 = 0; c0 < wl; c0 += 64) {
-        const int e = c0 + lane;
-        const int id = e < wl ? raw_id[e] : -1;
-        bool keep = id >= 0;
-        const uint32_t bit = 1u << (id & 31);
-        bool coll = false;
-        if (keep && (seen_bits[id >> 5] & bit)) keep = false;
-        if (keep) coll = (atomicOr(&seen_bits[id >> 5], bit) & bit) != 0u;
-        if (__ballot(coll)) {
-          bool dup = false;
-          for (int jl = 0; jl < 64; ++jl) {
-            const int idj = __shfl(id, jl, 64);
-            const int kj = __shfl((int)keep, jl, 64);
-            if (jl < lane && kj && idj == id) dup = true;
-          }
-          keep = keep && !dup;
-        }
-        const uint64_t km = __ballot(keep);
-        if (keep) {
-          const int p = count + __popcll(km & ((1ull << lane) - 1ull));
-          vis_phys[p] = raw_phys[e];
-          vis_j[p] = id;
-          vis_k[p] = k0 + e;
-        }
-        count += __popcll(km);
-      }
-      if (lane == 0) s_count = count;
-    }
-    __syncthreads();
-    const int nv = s_count;
-
-    // ---- ring prologue: gather pages 0 .. kRing-2, announce 0 .. kRing-3
-    const int pro = min(kRing - 1, nv);
-    for (int p = 0; p < pro; ++p) {
-      const int jp = __builtin_amdgcn_readfirstlane(vis_j[p]);
-      const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[p]) * a.kv_sp;
-      gather_page_share<NW, PW>(kbase + off, vbase + off, a.kv_st, ring_addr + (uint32_t)(p % kRing) * kPageBytes,
-                                min(kPage, L - jp * kPage), wave, lane);
-    }
-    for (int p = 0; p < min(kRing - 2, nv); ++p) {
-      wait_pages_outstanding<PW>(pro - 1 - p);
-      if (lane == 0) lds_add_release(&ready_ctr[p % kRing], 1);
-    }
-
-    for (int v = 0; v < nv; ++v) {
-      const int slot = v % kRing;
-      // ---- keep kRing-1 pages in flight: gather page v+kRing-1 once every wave is done
-      //      with the page that held its slot, then announce page v+kRing-2
-      const int u = v + kRing - 1;
-      const int issued = min(u, nv - 1);
-      if (u < nv) {
-        if (!wait_at_least(&used_ctr[u % kRing], NW * (u / kRing), &s_abort)) break;
-        const int ju = __builtin_amdgcn_readfirstlane(vis_j[u]);
-        const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(vis_phys[u]) * a.kv_sp;
-        gather_page_share<NW, PW>(kbase + off, vbase + off, a.kv_st, ring_addr + (uint32_t)(u % kRing) * kPageBytes,
-                                  min(kPage, L - ju * kPage), wave, lane);
-      }
-      const int sgn = v + kRing - 2;
-      if (sgn < nv) {
-        wait_pages_outstanding<PW>(issued - sgn);
-        if (lane == 0) lds_add_release(&ready_ctr[sgn % kRing], 1);
-      }
-      // ---- page v resident in its slot (every wave's share has landed)
-      if (!wait_at_least(&ready_ctr[slot], NW * (v / kRing + 1), &s_abort)) break;
-      const int j = __builtin_amdgcn_readfirstlane(vis_j[v]);
-      LDS_PTR(const uint8_t) kb = ring_lds + slot * kPageBytes;
-      LDS_PTR(const uint8_t) vb = kb + kTileBytes;
-      const int tail_rows = min(kPage, L - j * kPage);  // valid tokens on page j
-
-      // ---- S^T = K Q^T for 64 keys x 32 query rows (fp32 accumulate)
-      f32x16_t acc[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[tt][e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = tt * 32 + (lane & 31);
-          const bf16x8_t ka = *(LDS_PTR(const bf16x8_t))(kb + t * 256 + swz_k(t, 2 * c + hi) * 16);
-          acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[c], acc[tt], 0, 0, 0);
-        }
-      }
-      // ---- visibility on the diagonal and tail pages: t <= c and t < L
-      if (j == i || tail_rows < kPage) {
-        const int c_tok = i * kPage + r_blk;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int t = j * kPage + tt * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            if (t > c_tok || t >= L) acc[tt][e] = -INFINITY;
-          }
-      }
-      // ---- local row max, running-max update, block vote (Eq. (1), (2), (5))
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[tt][e]);
-      mx = permlane32_max(mx);
-      const float mloc2 = mx * scale_log2;
-      const float mnew2 = fmaxf(m2, mloc2);
-      const float dd = (row_ok && mloc2 != -INFINITY) ? (mloc2 - mnew2) : -INFINITY;
-      const float my_margin = max_lanes32(dd);
-      // exchange the 32-row partial margin with the other half of this head
-      const int par = v & 1;
-      if (lane == 0) {
-        vote_val[hl][half][par] = my_margin;
-        __hip_atomic_store(&vote_seq[hl][half][par], v + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      if (!wait_at_least(&vote_seq[hl][half ^ 1][par], v + 1, &s_abort)) break;
-      const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(
-                                                  __float_as_int(vote_val[hl][half ^ 1][par]))));
-      const bool skip = skip_on && (margin2 < tau2);
-      if (logging && half == 0 && lane == 0) {
-        dec_lds[hl][vis_k[v] - k0] = skip ? 1 : 0;
-        mar_lds[hl][vis_k[v] - k0] = margin2 * kLn2;
-      }
-      m2 = mnew2;
-      if (!skip) {
-        // ---- move the exponent base if some row's max passed it by more than kRebase
-        if (__ballot(m2 > b2 + kRebase)) {
-          const float alpha = (m2 == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(b2 - m2);
-          b2 = m2;
-          l2 *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[nt][e] *= alpha;
-        }
-        // ---- P = 2^(S' - b) as bf16 B operands; row sums; O^T += V^T P^T
-        const float msub = (b2 == -INFINITY) ? 0.f : b2;
-        bf16x8_t pb[4];
-        float rs = 0.f;
-#pragma unroll
-        for (int tc = 0; tc < 4; ++tc) {
-          bf16x8_t pv;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(acc[tc >> 1][8 * (tc & 1) + kk], scale_log2, -msub));
-            rs += p;
-            pv[kk] = (__bf16)p;
-          }
-          pb[tc] = pv;
-        }
-        l2 += permlane32_sum(rs);
-#pragma unroll
-        for (int tc = 0; tc < 4; ++tc) {
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const bf16x8_t va = read_vt(vb, nt, tc, lane);
-            o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[tc], o[nt], 0, 0, 0);
-          }
-        }
-      }
-      // every LDS read of this slot has returned (the release waits for the wave's
-      // outstanding LDS reads before the count moves)
-      if (lane == 0) lds_add_release(&used_ctr[slot], 1);
-    }
-    wait_vmcnt<0>();  // no page gather may still be writing LDS past this point
-    __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
-    if (logging && half == 0) {
-      uint8_t* drow = a.decisions + ((int64_t)qb * a.hq + h) * a.max_mask_len + k0;
-      float* mrw = a.margins ? a.margins + ((int64_t)qb * a.hq + h) * a.max_mask_len + k0 : nullptr;
-      for (int x = lane; x < wl; x += 64) {
-        drow[x] = dec_lds[hl][x];
-        if (mrw) mrw[x] = mar_lds[hl][x];
-      }
-    }
-    if (s_abort != 0) break;
-    __syncthreads();
+    w.raw_id[e] = ph >= 0 ? id : -1;
+    w.raw_phys[e] = ph;
   }
-  if (logging && half == 0) {
-    uint8_t* drow = a.decisions + ((int64_t)qb * a.hq + h) * a.max_mask_len;
-    float* mrw = a.margins ? a.margins + ((int64_t)qb * a.hq + h) * a.max_mask_len : nullptr;
-    for (int x = len + lane; x < a.max_mask_len; x += 64) {
-      drow[x] = 2;
-      if (mrw) mrw[x] = __builtin_nanf("");
+  __syncthreads();
+  // wave 0 compacts the visited entries in mask order
+  if (wave == 0) {
+    int count = 0;
+    for (int c0 = 0; c0 < wl; c0 += 64) {
+      const int e = c0 + lane;
+      const int id = e < wl ? w.raw_id[e] : -1;
+      bool keep = id >= 0;
+      const uint32_t bit = 1u << (id & 31);
+      bool coll = false;
+      if (keep && (w.seen_bits[id >> 5] & bit)) keep = false;
+      if (keep) coll = (atomicOr(&w.seen_bits[id >> 5], bit) & bit) != 0u;
+      if (__ballot(coll)) {
+        // a repeated id inside these 64 entries: the lowest entry keeps it
+        bool dup = false;
+        for (int jl = 0; jl < 64; ++jl) {
+          const int idj = __shfl(id, jl, 64);
+          const int kj = __shfl((int)keep, jl, 64);
+          if (jl < lane && kj && idj == id) dup = true;
+        }
+        keep = keep && !dup;
+      }
+      const uint64_t km = __ballot(keep);
+      if (keep) {
+        const int p = count + __popcll(km & ((1ull << lane) - 1ull));
+        w.vis_phys[p] = w.raw_phys[e];
+        w.vis_j[p] = id;
+        w.vis_k[p] = k0 + e;
+      }
+      count += __popcll(km);
     }
+    if (lane == 0) w.count = count;
   }
-  if (threadIdx.x == 0 && s_abort != 0) atomicAdd(a.error_count, 1);
+  __syncthreads();
+  return w.count;
+}
 
-  // ---- epilogue: O <- O / l (0 when nothing was computed), bf16 out, natural-log LSE
+// S^T = K Q^T for the 64 keys of the K tile at kb and the wave's 32 query rows.
+// All 16 K operands are requested ahead of the MFMAs, so LDS latency is paid
+// once per tile rather than once per MFMA.
+__device__ __forceinline__ void qk_tile(uint32_t kb, const bf16x8_t (&qf)[8], int lane,
+                                        f32x16_t (&acc)[2]) {
+  const uint32_t kl = k_lane_base(kb, lane);
+  bf16x8_t ka[8][2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) ka[c][tt] = *lds_at<bf16x8_t>((kl ^ (uint32_t)(c << 5)) + (uint32_t)tt * 8192u);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[tt][e] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c][tt], qf[c], acc[tt], 0, 0, 0);
+  // keep the scheduler from sinking each read next to its MFMA: 8 reads ahead
+#pragma unroll
+  for (int x = 0; x < 8; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+// Visibility on the diagonal and tail pages: t <= c and t < L.
+__device__ __forceinline__ void mask_tile(f32x16_t (&acc)[2], int j, int i, int r_blk, int L, int hi) {
+  if (j == i || L - j * kPage < kPage) {
+    const int c_tok = i * kPage + r_blk;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = j * kPage + tt * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        if (t > c_tok || t >= L) acc[tt][e] = -INFINITY;
+      }
+  }
+}
+// The page's local row max in the scaled log2 domain; lanes l and l^32 hold the
+// same row.
+__device__ __forceinline__ float rowmax2(const f32x16_t (&acc)[2], float scale_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[tt][e]);
+  return permlane32_max(mx) * scale_log2;
+}
+__device__ __forceinline__ float mask_rowmax2(f32x16_t (&acc)[2], int j, int i, int r_blk, int L, int hi,
+                                              float scale_log2) {
+  mask_tile(acc, j, i, r_blk, L, hi);
+  return rowmax2(acc, scale_log2);
+}
+
+// P = 2^(S' - b) as bf16 B operands (lane's 32 logits of its row, key order of
+// the S^T accumulator), returning the lane's partial row sum.
+__device__ __forceinline__ float probs_tile(const f32x16_t (&acc)[2], float scale_log2, float b2,
+                                            bf16x8_t (&pb)[4]) {
+  const float msub = (b2 == -INFINITY) ? 0.f : b2;
+  float rs = 0.f;
+#pragma unroll
+  for (int tc = 0; tc < 4; ++tc) {
+    bf16x8_t pv;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(acc[tc >> 1][8 * (tc & 1) + kk], scale_log2, -msub));
+      rs += p;
+      pv[kk] = (__bf16)p;
+    }
+    pb[tc] = pv;
+  }
+  return rs;
+}
+
+// The 16 V^T A operands of the V tile at vb.
+__device__ __forceinline__ void load_vt_tile(uint32_t vb, int lane, bf16x8_t (&va)[4][4]) {
+  const uint32_t vl = v_lane_base(vb, lane);
+#pragma unroll
+  for (int tc = 0; tc < 4; ++tc)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) va[tc][nt] = read_vt(vl, nt, tc);
+}
+// O^T += V^T P^T from operands in registers.
+__device__ __forceinline__ void pv_mfma(const bf16x8_t (&va)[4][4], const bf16x8_t (&pb)[4], f32x16_t (&o)[4]) {
+#pragma unroll
+  for (int tc = 0; tc < 4; ++tc)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[tc][nt], pb[tc], o[nt], 0, 0, 0);
+}
+// O^T += V^T P^T for the V tile at vb.
+__device__ __forceinline__ void pv_tile(uint32_t vb, const bf16x8_t (&pb)[4], int lane,
+                                        f32x16_t (&o)[4]) {
+  bf16x8_t va[4][4];
+  load_vt_tile(vb, lane, va);
+  pv_mfma(va, pb, o);
+}
+// Move the exponent base when some row's running max passed it by more than
+// kRebase (O / l does not depend on the base), rescaling l and O.
+__device__ __forceinline__ void maybe_rebase(float m2, float& b2, float& l2, f32x16_t (&o)[4]) {
+  if (__ballot(m2 > b2 + kRebase)) {
+    const float alpha = (m2 == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(b2 - m2);
+    b2 = m2;
+    l2 *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[nt][e] *= alpha;
+  }
+}
+
+// Decision and margin log of one head for mask entries k0 .. k0+wl-1.
+__device__ __forceinline__ void flush_log(const PrefillArgs& a, const Unit& u, int k0, int wl, const uint8_t* dec,
+                                          const float* mar, int lane) {
+  uint8_t* drow = a.decisions + ((int64_t)u.qb * a.hq + u.h) * a.max_mask_len + k0;
+  float* mrw = a.margins ? a.margins + ((int64_t)u.qb * a.hq + u.h) * a.max_mask_len + k0 : nullptr;
+  for (int x = lane; x < wl; x += 64) {
+    drow[x] = dec[x];
+    if (mrw) mrw[x] = mar[x];
+  }
+}
+// Entries past the mask length: code 2 (not visited), margin NaN.
+__device__ __forceinline__ void fill_log_tail(const PrefillArgs& a, const Unit& u, int lane) {
+  uint8_t* drow = a.decisions + ((int64_t)u.qb * a.hq + u.h) * a.max_mask_len;
+  float* mrw = a.margins ? a.margins + ((int64_t)u.qb * a.hq + u.h) * a.max_mask_len : nullptr;
+  for (int x = u.len + lane; x < a.max_mask_len; x += 64) {
+    drow[x] = 2;
+    if (mrw) mrw[x] = __builtin_nanf("");
+  }
+}
+
+// O <- O / l (0 when nothing was computed), bf16 out, natural-log LSE.
+__device__ __forceinline__ void store_output(const PrefillArgs& a, const Unit& u, const f32x16_t (&o)[4], float l2,
+                                             float b2, int r_blk, bool row_ok, int lane) {
+  const int hi = lane >> 5;
   const float inv_l = l2 > 0.f ? 1.f / l2 : 0.f;
-  uint16_t* orow = a.out + (int64_t)(tok0 + i * kPage + r_blk) * a.o_st + (int64_t)h * a.o_sh;
+  uint16_t* orow = a.out + (int64_t)(u.tok0 + u.i * kPage + r_blk) * a.o_st + (int64_t)u.h * a.o_sh;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const f32x16_t ov = o[nt] * inv_l;
@@ -576,7 +587,162 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_kernel(const PrefillArgs
     }
   }
   if (a.lse != nullptr && hi == 0 && row_ok)
-    a.lse[(int64_t)(tok0 + i * kPage + r_blk) * a.hq + h] = l2 > 0.f ? (b2 + log2f(l2)) * kLn2 : -INFINITY;
+    a.lse[(int64_t)(u.tok0 + u.i * kPage + r_blk) * a.hq + u.h] = l2 > 0.f ? (b2 + log2f(l2)) * kLn2 : -INFINITY;
+}
+
+__device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
+  return a.delta > 0.f ? (float)(log2((double)a.delta) - log2((double)L)) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// ring kernel: 1 or 2 q heads per workgroup (GQA groups of 1, 2, 3, 5, ...)
+// ---------------------------------------------------------------------------
+// Two waves per head (32 rows each).  K and V page tiles share one ring of kRing
+// page slots; every wave gathers its share of each page kRing-1 visits ahead.
+// LDS counters say when a slot's page has landed (ready) and when every wave is
+// done with it (used), so a head that skips a page runs ahead of one that
+// computes it.  The two halves of a head combine their partial vote margins
+// through LDS.  Every inter-wave wait is bounded: a wait that runs out sets the
+// workgroup's abort flag and the workgroup is counted in the health word.
+template <int HW>
+__global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const PrefillArgs a, int heads_per_group,
+                                                                    int nsub) {
+  constexpr int NW = 2 * HW;   // waves
+  constexpr int NT = 64 * NW;  // threads
+  constexpr int PW = 32 / NW;  // page-gather instructions per wave per page
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
+  __shared__ WindowLds wlds;
+  __shared__ uint8_t dec_lds[HW][kWindow];
+  __shared__ float mar_lds[HW][kWindow];
+  __shared__ int ready_ctr[kRing];
+  __shared__ int used_ctr[kRing];
+  __shared__ int vote_seq[HW][2][2];
+  __shared__ float vote_val[HW][2][2];
+  __shared__ int s_abort;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
+  const int half = wave & 1;  // rows 32*half .. +31 of the block; the halves of a head sit on different SIMDs
+  const int hl = wave >> 1;   // head within the workgroup
+  const Unit u = decode_unit<HW>(a, heads_per_group, nsub, hl);
+  const bool skip_on = a.delta > 0.f;
+  const float scale_log2 = a.sm_scale * kLog2e;
+  const float tau2 = skip_threshold2(a, u.L);
+  const bool logging = a.decisions != nullptr;
+  LDS_PTR(uint8_t) ring_lds = (LDS_PTR(uint8_t))ring;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring_lds;
+
+  const int r_blk = half * 32 + (lane & 31);
+  const bool row_ok = (u.i * kPage + r_blk) < u.L;
+  bf16x8_t qf[8];
+  load_q(a, u, r_blk, row_ok, lane >> 5, qf);
+
+  // ---- online-softmax state (log2 domain, scaled).  m2: the running row max of Eq. (2),
+  //      which the skip vote uses.  b2: the exponent base of l2 and O; it follows m2 lazily
+  //      (moved only when m2 exceeds it by more than kRebase, so p = 2^(s - b2) <= 2^kRebase)
+  //      -- O / l is unchanged by the choice of base, and the rescale of O becomes rare.
+  float m2 = -INFINITY, b2 = -INFINITY, l2 = 0.f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[nt][e] = 0.f;
+
+  for (int x = threadIdx.x; x < (u.n_pages + 31) / 32; x += NT) wlds.seen_bits[x] = 0u;
+  if (threadIdx.x == 0) s_abort = 0;
+
+  const int32_t* mrow = a.order_mask + ((int64_t)u.qb * a.hkv + u.g) * a.max_mask_len;
+  const uint16_t* kbase = a.k + (int64_t)u.g * a.kv_sh;
+  const uint16_t* vbase = a.v + (int64_t)u.g * a.kv_sh;
+  TileGather<NW> tg;
+  tg.init(a.kv_st, wave, lane);
+
+  for (int k0 = 0; k0 < u.len; k0 += kWindow) {
+    const int wl = min(kWindow, u.len - k0);
+    if (logging && half == 0)
+      for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
+    if (threadIdx.x < kRing) { ready_ctr[threadIdx.x] = 0; used_ctr[threadIdx.x] = 0; }
+    if (threadIdx.x < 4 * HW) (&vote_seq[0][0][0])[threadIdx.x] = 0;
+    const int nv = resolve_window<NT>(a, u, mrow, k0, wl, wlds, wave, lane);
+    auto gather = [&](int p) {
+      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]);
+      const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(wlds.vis_phys[p]) * a.kv_sp;
+      const uint32_t slot = ring_addr + (uint32_t)(p % kRing) * kPageBytes;
+      const int valid_rows = u.L - jp * kPage;
+      tg.issue(kbase + off, slot, valid_rows, false, wave, lane);
+      tg.issue(vbase + off, slot + kTileBytes, valid_rows, true, wave, lane);
+    };
+
+    // ---- ring prologue: gather pages 0 .. kRing-2, announce 0 .. kRing-3
+    const int pro = min(kRing - 1, nv);
+    for (int p = 0; p < pro; ++p) gather(p);
+    for (int p = 0; p < min(kRing - 2, nv); ++p) {
+      wait_pages_outstanding<PW>(pro - 1 - p);
+      if (lane == 0) lds_add_release(&ready_ctr[p % kRing], 1);
+    }
+
+    for (int v = 0; v < nv; ++v) {
+      const int slot = v % kRing;
+      // ---- keep kRing-1 pages in flight: gather page v+kRing-1 once every wave is done
+      //      with the page that held its slot, then announce page v+kRing-2
+      const int un = v + kRing - 1;
+      const int issued = min(un, nv - 1);
+      if (un < nv) {
+        if (!wait_at_least(&used_ctr[un % kRing], NW * (un / kRing), &s_abort)) break;
+        gather(un);
+      }
+      const int sgn = v + kRing - 2;
+      if (sgn < nv) {
+        wait_pages_outstanding<PW>(issued - sgn);
+        if (lane == 0) lds_add_release(&ready_ctr[sgn % kRing], 1);
+      }
+      // ---- page v resident in its slot (every wave's share has landed)
+      if (!wait_at_least(&ready_ctr[slot], NW * (v / kRing + 1), &s_abort)) break;
+      const int j = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      const uint32_t kb = ring_addr + (uint32_t)slot * kPageBytes;
+      const uint32_t vb = kb + kTileBytes;
+
+      f32x16_t acc[2];
+      qk_tile(kb, qf, lane, acc);
+      // ---- running-max update and block vote (Eq. (1), (2), (5))
+      const float mloc2 = mask_rowmax2(acc, j, u.i, r_blk, u.L, lane >> 5, scale_log2);
+      const float mnew2 = fmaxf(m2, mloc2);
+      const float dd = (row_ok && mloc2 != -INFINITY) ? (mloc2 - mnew2) : -INFINITY;
+      const float my_margin = max_lanes32(dd);
+      // exchange the 32-row partial margin with the other half of this head
+      const int par = v & 1;
+      if (lane == 0) {
+        vote_val[hl][half][par] = my_margin;
+        __hip_atomic_store(&vote_seq[hl][half][par], v + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (!wait_at_least(&vote_seq[hl][half ^ 1][par], v + 1, &s_abort)) break;
+      const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(
+                                                  __float_as_int(vote_val[hl][half ^ 1][par]))));
+      const bool skip = skip_on && (margin2 < tau2);
+      if (logging && half == 0 && lane == 0) {
+        dec_lds[hl][wlds.vis_k[v] - k0] = skip ? 1 : 0;
+        mar_lds[hl][wlds.vis_k[v] - k0] = margin2 * kLn2;
+      }
+      m2 = mnew2;
+      if (!skip) {
+        maybe_rebase(m2, b2, l2, o);
+        bf16x8_t pb[4];
+        l2 += permlane32_sum(probs_tile(acc, scale_log2, b2, pb));
+        pv_tile(vb, pb, lane, o);
+      }
+      // every LDS read of this slot has returned (the release waits for the wave's
+      // outstanding LDS reads before the count moves)
+      if (lane == 0) lds_add_release(&used_ctr[slot], 1);
+    }
+    wait_vmcnt<0>();  // no page gather may still be writing LDS past this point
+    __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
+    if (logging && half == 0) flush_log(a, u, k0, wl, dec_lds[hl], mar_lds[hl], lane);
+    if (s_abort != 0) break;
+    __syncthreads();
+  }
+  if (logging && half == 0) fill_log_tail(a, u, lane);
+  if (threadIdx.x == 0 && s_abort != 0) atomicAdd(a.error_count, 1);
+  store_output(a, u, o, l2, b2, r_blk, row_ok, lane);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -590,11 +756,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)a.total_qblocks * (unsigned)a.hkv * (unsigned)nsub);
   if (HW == 4)
-    hipLaunchKernelGGL(osk_prefill_kernel<4>, grid, dim3(512), 0, stream, a, G, nsub);
+    hipLaunchKernelGGL(osk_prefill_ring_kernel<4>, grid, dim3(512), 0, stream, a, G, nsub);
   else if (HW == 2)
-    hipLaunchKernelGGL(osk_prefill_kernel<2>, grid, dim3(256), 0, stream, a, G, nsub);
+    hipLaunchKernelGGL(osk_prefill_ring_kernel<2>, grid, dim3(256), 0, stream, a, G, nsub);
   else
-    hipLaunchKernelGGL(osk_prefill_kernel<1>, grid, dim3(128), 0, stream, a, G, nsub);
+    hipLaunchKernelGGL(osk_prefill_ring_kernel<1>, grid, dim3(128), 0, stream, a, G, nsub);
   return hipGetLastError();
 }
 

@@ -32,8 +32,9 @@
  * - Supported: head_dim = 128, page_size = 64 (the query block equals the KV
  *   page), bfloat16 Q/K/V/out, num_q_heads % num_kv_heads == 0.
  *   Limits: total_qblocks <= 16384, max_mask_len <= 8191,
- *   max_pages_per_seq <= 16384 (<= 8192 for the mask builder).  Anything else
- *   returns COSA_ERR_UNSUPPORTED.
+ *   max_pages_per_seq <= 16384 (<= 8192 for the mask builder),
+ *   kv_stride_tok <= 2^24 elements (a page's byte offsets fit in 32 bits).
+ *   Anything else returns COSA_ERR_UNSUPPORTED.
  * - Layouts (element strides; head_dim is contiguous; strides are multiples of
  *   8 elements and the base pointers are 16-byte aligned):
  *     q, out        [total_q_tokens, num_q_heads, 128]   (sequences packed on T)

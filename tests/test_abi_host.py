@@ -62,6 +62,7 @@ def test_check_args_status_codes():
         (dict(q_stride_head=100), INVALID), (dict(kv_stride_tok=0), INVALID),
         (dict(total_q_tokens=64 * 64 + 1), INVALID), (dict(total_qblocks=65, total_q_tokens=64), INVALID),
         (dict(reserved=1), INVALID), (dict(sm_scale=float("nan")), INVALID),
+        (dict(kv_stride_tok=(1 << 24) + 8), UNSUPPORTED), (dict(kv_stride_tok=1 << 24), OK),
     ]
     for kw, want in cases:
         dd = good_dims(**kw)
