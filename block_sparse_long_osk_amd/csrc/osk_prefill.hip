@@ -129,11 +129,14 @@ __device__ __forceinline__ void lds_add_release(int* p, int v) {
 // Bounded wait until *ctr >= target.  Every wave of the workgroup is resident,
 // and each counter is advanced by waves that never wait on a later visit, so
 // the wait ends; the bound turns a broken protocol into an abort, never a hang.
+// The counter is polled back to back (one LDS round trip per poll); the abort
+// flag is checked every 64 polls and the wave sleeps between polls only once a
+// wait has lasted 256 polls.
 __device__ __forceinline__ bool wait_at_least(int* ctr, int target, int* abort_flag) {
   for (int it = 0; it < kSpinLimit; ++it) {
     if (__builtin_amdgcn_readfirstlane(lds_load_acquire(ctr)) >= target) return true;
-    if (__builtin_amdgcn_readfirstlane(lds_load_acquire(abort_flag)) != 0) return false;
-    __builtin_amdgcn_s_sleep(1);
+    if ((it & 63) == 63 && __builtin_amdgcn_readfirstlane(lds_load_acquire(abort_flag)) != 0) return false;
+    if (it >= 256) __builtin_amdgcn_s_sleep(1);
   }
   __hip_atomic_store(abort_flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   return false;
