@@ -531,6 +531,7 @@ __device__ __forceinline__ void pv_tile(uint32_t vb, const bf16x8_t (&pb)[4], in
   load_vt_tile(vb, lane, va);
   pv_mfma(va, pb, o);
 }
+
 // Move the exponent base when some row's running max passed it by more than
 // kRebase (O / l does not depend on the base), rescaling l and O.
 __device__ __forceinline__ void maybe_rebase(float m2, float& b2, float& l2, f32x16_t (&o)[4]) {
@@ -712,15 +713,20 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       const float mnew2 = fmaxf(m2, mloc2);
       const float dd = (row_ok && mloc2 != -INFINITY) ? (mloc2 - mnew2) : -INFINITY;
       const float my_margin = max_lanes32(dd);
-      // exchange the 32-row partial margin with the other half of this head
+      // exchange the 32-row partial margin with the other half of this head (needed
+      // only when pages can be skipped or the decisions are logged)
+      const bool vote = skip_on || logging;
       const int par = v & 1;
-      if (lane == 0) {
+      if (vote && lane == 0) {
         vote_val[hl][half][par] = my_margin;
         __hip_atomic_store(&vote_seq[hl][half][par], v + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      if (!wait_at_least(&vote_seq[hl][half ^ 1][par], v + 1, &s_abort)) break;
-      const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(
-                                                  __float_as_int(vote_val[hl][half ^ 1][par]))));
+      float margin2 = my_margin;
+      if (vote) {
+        if (!wait_at_least(&vote_seq[hl][half ^ 1][par], v + 1, &s_abort)) break;
+        margin2 = fmaxf(my_margin,
+                        __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vote_val[hl][half ^ 1][par]))));
+      }
       const bool skip = skip_on && (margin2 < tau2);
       if (logging && half == 0 && lane == 0) {
         dec_lds[hl][wlds.vis_k[v] - k0] = skip ? 1 : 0;
