@@ -107,6 +107,41 @@ def cpu_baseline(batch, wl, delta, budget_s=15.0):
             "seconds": round(spent, 2)}
 
 
+def skip_sweep(args, wl, db, om, ml):
+    """Skip ratio and ms per call against Delta for two visit orders of the same page sets:
+    the proxy's (score descending) and ascending page id.  tau = ln(Delta / L) is swept over a
+    fixed grid; the pages' own Delta = 2000 is included."""
+    import numpy as np
+    import torch
+    from block_sparse_long_osk_amd import runner
+    width = om.shape[2]
+    om_h = om.cpu().numpy()
+    ml_h = ml.cpu().numpy()
+    asc = om_h.copy()
+    for idx in np.ndindex(ml_h.shape):
+        n = int(ml_h[idx])
+        asc[idx][:n] = np.sort(asc[idx][:n])
+    orders = {"proxy": (om, ml), "ascending": runner.upload_mask(asc, ml_h)}
+    L = max(wl.seq_lens)
+    deltas = [("tau", float(L * np.exp(t)), t) for t in (-1.0, -0.5, -0.3, -0.2, -0.15, -0.1, -0.05, -0.02, 0.0)]
+    deltas.append(("pages_delta", 2000.0, float(np.log(2000.0 / L))))
+    outs = runner.allocate_outputs(db, width, log=False)
+    outs.lse = None
+    ws = runner.workspace_for(db, width)
+    for kind, delta, tau in deltas:
+        row = {"mode": "skip-sweep", "workload": wl.name, "delta": delta, "tau_at_longest_seq": tau, "kind": kind}
+        for name, (m, mlen) in orders.items():
+            logged = runner.prefill(db, m, mlen, delta, log=True)
+            torch.cuda.synchronize()
+            dec = logged.decisions
+            visited = int((dec != 2).sum().item())
+            skipped = int((dec == 1).sum().item())
+            del logged, dec
+            per, _ = time_calls(lambda: runner.prefill(db, m, mlen, delta, outputs=outs, workspace=ws), 5, 2)
+            row[name] = {"skip_ratio": skipped / max(visited, 1), "ms_per_layer": statistics.median(per)}
+        print(json.dumps(row), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,9 +151,11 @@ def main():
     ap.add_argument("--workload", default="cfg4_128k_structured")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "counters"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "counters", "skip-sweep"], default="bench",
                     help="counters: a plain 1 GiB device copy (the counter scale reference), then "
-                         "--steps OSK calls; for rocprofv3 --pmc passes")
+                         "--steps OSK calls; for rocprofv3 --pmc passes.  skip-sweep: in-kernel skip "
+                         "ratio and time per call against Delta, with the proxy's visit order and with "
+                         "every mask row sorted ascending (one JSON line per Delta)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the kernel shards by KV head or by "
@@ -150,6 +187,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"mode": "counters", "workload": wl.name, "copy_bytes": 1 << 30,
                           "osk_calls": args.steps, "kernel_source_hash": kernel_source_hash()}))
+        return
+    if args.mode == "skip-sweep":
+        skip_sweep(args, wl, db, om, ml)
         return
     width = om.shape[2]
     ws_b = torch.empty(binding.cosa_build_order_mask_workspace_bytes(db.dims(width)), dtype=torch.uint8,
