@@ -8,9 +8,9 @@
 // query representation of KV head g sums the group's per-head block means.
 //
 // Kernels:
-//   pool   one workgroup per (query block, KV head), one thread per dim:
+//   pool   one workgroup per (query block, KV head):
 //          qbar = sum_h mean_r q, kbar = mean_t k of the same-index logical page;
-//          Q and K are each read once, coalesced along the head dimension.
+//          Q and K are each read once in 16-byte chunks along the head dimension.
 //   select one workgroup per (query block, KV head): fp32 scores for the causal
 //          pages, forced pages set aside, a bitonic sort of the rest by
 //          (score desc, id asc) in LDS, and a merge of the forced pages into the
@@ -34,31 +34,59 @@ __device__ __forceinline__ int seq_of_qblock(const int32_t* cu_qblocks, int num_
   return lo;
 }
 
-__global__ __launch_bounds__(128) void mask_pool_kernel(const BuilderArgs a) {
-  const int qb = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
+// Thread t handles dims 8*(t%16) .. +8 (one 16-byte load per row) of rows
+// t/16, t/16 + 16, ...; the 16 row groups' partial sums are combined in LDS.
+__global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
+  __shared__ float red[16][kHeadDim];
+  const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int chunk = tid & 15, rg = tid >> 4;
   const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
   const int i = qb - a.cu_qblocks[s];
   const int tok0 = a.cu_seqlens[s];
   const int L = a.cu_seqlens[s + 1] - tok0;
   const int rows = min(kPage, L - i * kPage);
   const int G = a.hq / a.hkv;
-  float acc = 0.f;
+  auto add8 = [](float (&acc)[8], const uint16_t* p) {
+    const uint4 w = *(const uint4*)p;
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(u[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(u[e] & 0xffff0000u);
+    }
+  };
+  // ---- qbar: sum over the group's heads of the block mean
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    float sh = 0.f;
-    for (int r = 0; r < rows; ++r)
-      sh += bf16_bits_to_float(a.q[(int64_t)(tok0 + i * kPage + r) * a.q_st + (int64_t)h * a.q_sh + d]);
-    acc += sh / (float)rows;
+    const uint16_t* qh = a.q + (int64_t)tok0 * a.q_st + (int64_t)(g * G + hh) * a.q_sh + chunk * 8;
+    for (int r = rg; r < rows; r += 16) add8(acc, qh + (int64_t)(i * kPage + r) * a.q_st);
   }
-  a.qbar[((int64_t)qb * a.hkv + g) * kHeadDim + d] = acc;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][chunk * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float t = 0.f;
+    for (int x = 0; x < 16; ++x) t += red[x][tid];
+    a.qbar[((int64_t)qb * a.hkv + g) * kHeadDim + tid] = t / (float)rows;
+  }
+  __syncthreads();
+  // ---- kbar: mean of the same-index logical page's keys
   const int ph = i < a.max_pages ? a.page_table[(int64_t)s * a.max_pages + i] : -1;
-  float ks = 0.f;
-  if (ph >= 0 && ph < a.num_phys) {
-    const uint16_t* kp = a.k + (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + d;
-    for (int t = 0; t < rows; ++t) ks += bf16_bits_to_float(kp[(int64_t)t * a.kv_st]);
-    ks /= (float)rows;
+  const bool has_page = ph >= 0 && ph < a.num_phys;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  if (has_page) {
+    const uint16_t* kp = a.k + (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + chunk * 8;
+    for (int t = rg; t < rows; t += 16) add8(acc, kp + (int64_t)t * a.kv_st);
   }
-  a.kbar[((int64_t)qb * a.hkv + g) * kHeadDim + d] = ks;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][chunk * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float t = 0.f;
+    for (int x = 0; x < 16; ++x) t += red[x][tid];
+    a.kbar[((int64_t)qb * a.hkv + g) * kHeadDim + tid] = has_page ? t / (float)rows : 0.f;
+  }
 }
 
 // ceil(b1 * n - 1e-3) clamped to [0, n]
@@ -75,9 +103,10 @@ __device__ __forceinline__ uint64_t sort_key(float score, int id) {
   return ((uint64_t)(~ord) << 32) | (uint32_t)id;
 }
 
+// keys: dynamic LDS of the launch's key capacity (a power of two >= max_pages_per_seq)
 __global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
   __shared__ float qs[kHeadDim];
-  __shared__ uint64_t keys[kMaxPagesBuilder];
+  extern __shared__ uint64_t keys[];
   __shared__ uint64_t fkeys[2];
   const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
@@ -155,10 +184,13 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
 hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream) {
   if (a.total_qblocks == 0) return hipSuccess;
   const dim3 grid((unsigned)a.total_qblocks, (unsigned)a.hkv);
-  hipLaunchKernelGGL(mask_pool_kernel, grid, dim3(kHeadDim), 0, stream, a);
+  hipLaunchKernelGGL(mask_pool_kernel, grid, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(mask_select_kernel, grid, dim3(256), 0, stream, a);
+  // sort keys in LDS sized for the longest row (fewer workgroups per CU otherwise)
+  int cap = 1;
+  while (cap < a.max_pages) cap <<= 1;
+  hipLaunchKernelGGL(mask_select_kernel, grid, dim3(256), (size_t)cap * sizeof(uint64_t), stream, a);
   return hipGetLastError();
 }
 
