@@ -148,9 +148,19 @@ int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t
   return width;
 }
 
+// builder workspace: pooled query and key proxies [total_qblocks, Hkv, 128] fp32 each,
+// then the score rows [total_qblocks, Hkv, max_pages_per_seq] fp32
+static size_t builder_pool_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * kHeadDim * sizeof(float) + 1);
+}
+static size_t builder_score_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)(d->max_pages_per_seq > 0 ? d->max_pages_per_seq : 0) *
+                      sizeof(float) + 1);
+}
+
 size_t cosa_build_order_mask_workspace_bytes(const cosa_osk_dims_t* dims) {
   if (dims == nullptr || dims->total_qblocks < 0 || dims->num_kv_heads < 1) return 0;
-  return 2 * round_up((size_t)dims->total_qblocks * dims->num_kv_heads * kHeadDim * sizeof(float) + 1);
+  return 2 * builder_pool_bytes(dims) + builder_score_bytes(dims);
 }
 
 cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
@@ -179,7 +189,10 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   a.mask_len = mask_len;
   a.scores = proxy_scores;
   a.qbar = static_cast<float*>(workspace);
-  a.kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  a.kbar = reinterpret_cast<float*>(static_cast<char*>(workspace) + builder_pool_bytes(dims));
+  a.score_rows = proxy_scores != nullptr
+                     ? proxy_scores
+                     : reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * builder_pool_bytes(dims));
   a.q_st = dims->q_stride_tok;
   a.q_sh = dims->q_stride_head;
   a.kv_sp = dims->kv_stride_page;

@@ -11,10 +11,12 @@
 //   pool   one workgroup per (query block, KV head):
 //          qbar = sum_h mean_r q, kbar = mean_t k of the same-index logical page;
 //          Q and K are each read once in 16-byte chunks along the head dimension.
-//   select one workgroup per (query block, KV head): fp32 scores for the causal
-//          pages, forced pages set aside, a bitonic sort of the rest by
-//          (score desc, id asc) in LDS, and a merge of the forced pages into the
-//          top n_keep by the same key.
+//   score  one workgroup per 8 consecutive query blocks of a sequence and a KV
+//          head: fp32 scores of the causal pages, each pooled key row read once
+//          for the 8 blocks; rows go to the caller's proxy_scores or workspace.
+//   select one workgroup per (query block, KV head): forced pages set aside, a
+//          bitonic sort of the rest by (score desc, id asc) in LDS, and a merge of
+//          the forced pages into the top n_keep by the same key.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -89,6 +91,55 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
   }
 }
 
+// Query blocks per score workgroup: each pooled key row is read once for the group.
+constexpr int kScoreGroup = 8;
+
+// score_j = qbar . kbar_j (fp32, dims in order) for the causal pages j <= i of
+// kScoreGroup consecutive query blocks of one sequence and KV head; rows are
+// written for j <= i only.
+__global__ __launch_bounds__(256) void mask_score_kernel(const BuilderArgs a) {
+  __shared__ float qs[kScoreGroup][kHeadDim];
+  const int gi = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  // the sequence of group gi (groups do not straddle sequences)
+  int s = 0, base = 0;
+  for (; s < a.num_seqs; ++s) {
+    const int ng = (a.cu_qblocks[s + 1] - a.cu_qblocks[s] + kScoreGroup - 1) / kScoreGroup;
+    if (gi < base + ng) break;
+    base += ng;
+  }
+  if (s >= a.num_seqs) return;  // the grid is an upper bound on the group count
+  const int qb0 = a.cu_qblocks[s];
+  const int i0 = (gi - base) * kScoreGroup;
+  const int ng = min(kScoreGroup, a.cu_qblocks[s + 1] - qb0 - i0);
+  for (int x = tid; x < kScoreGroup * kHeadDim; x += 256) {
+    const int q = x / kHeadDim, d = x % kHeadDim;
+    qs[q][d] = q < ng ? a.qbar[((int64_t)(qb0 + i0 + q) * a.hkv + g) * kHeadDim + d] : 0.f;
+  }
+  __syncthreads();
+  // block indices are clamped to the page-table width as in the select kernel
+  const int jmax = min(i0 + ng - 1, a.max_pages - 1);
+  for (int j = tid; j <= jmax; j += 256) {
+    const float* kb = a.kbar + ((int64_t)(qb0 + j) * a.hkv + g) * kHeadDim;
+    float acc[kScoreGroup];
+#pragma unroll
+    for (int q = 0; q < kScoreGroup; ++q) acc[q] = 0.f;
+    for (int d = 0; d < kHeadDim; d += 4) {
+      const float4 kv = *(const float4*)(kb + d);
+#pragma unroll
+      for (int q = 0; q < kScoreGroup; ++q) {
+        acc[q] = fmaf(qs[q][d], kv.x, acc[q]);
+        acc[q] = fmaf(qs[q][d + 1], kv.y, acc[q]);
+        acc[q] = fmaf(qs[q][d + 2], kv.z, acc[q]);
+        acc[q] = fmaf(qs[q][d + 3], kv.w, acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kScoreGroup; ++q)
+      if (q < ng && j <= min(i0 + q, a.max_pages - 1))
+        a.score_rows[((int64_t)(qb0 + i0 + q) * a.hkv + g) * a.max_pages + j] = acc[q];
+  }
+}
+
 // ceil(b1 * n - 1e-3) clamped to [0, n]
 __device__ __forceinline__ int keep_count(float b1, int n) {
   if (n <= 0) return 0;
@@ -105,7 +156,6 @@ __device__ __forceinline__ uint64_t sort_key(float score, int id) {
 
 // keys: dynamic LDS of the launch's key capacity (a power of two >= max_pages_per_seq)
 __global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
-  __shared__ float qs[kHeadDim];
   extern __shared__ uint64_t keys[];
   __shared__ uint64_t fkeys[2];
   const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
@@ -113,8 +163,6 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
   // block index within the sequence; the clamp keeps the candidate list inside the
   // LDS key array even for a cu_qblocks inconsistent with max_pages_per_seq
   const int i = min(qb - a.cu_qblocks[s], a.max_pages - 1);
-  const int qb0 = a.cu_qblocks[s];
-  if (tid < kHeadDim) qs[tid] = a.qbar[((int64_t)qb * a.hkv + g) * kHeadDim + tid];
   const bool f_first = (a.flags & 1u) != 0u;
   const bool f_diag = (a.flags & 2u) != 0u && !(f_first && i == 0);
   const int nf = (f_first ? 1 : 0) + (f_diag ? 1 : 0);
@@ -122,19 +170,9 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
   const int nkeep = keep_count(a.budget1, nrest);
   int N = 1;
   while (N < nrest) N <<= 1;
-  __syncthreads();
+  const float* srow = a.score_rows + ((int64_t)qb * a.hkv + g) * a.max_pages;
   for (int j = tid; j <= i; j += 256) {
-    const float* kb = a.kbar + ((int64_t)(qb0 + j) * a.hkv + g) * kHeadDim;
-    float sc = 0.f;
-    for (int d = 0; d < kHeadDim; d += 4) {
-      const float4 kv = *(const float4*)(kb + d);
-      sc = fmaf(qs[d], kv.x, sc);
-      sc = fmaf(qs[d + 1], kv.y, sc);
-      sc = fmaf(qs[d + 2], kv.z, sc);
-      sc = fmaf(qs[d + 3], kv.w, sc);
-    }
-    if (a.scores) a.scores[((int64_t)qb * a.hkv + g) * a.max_pages + j] = sc;
-    const uint64_t key = sort_key(sc, j);
+    const uint64_t key = sort_key(srow[j], j);
     if (f_first && j == 0) fkeys[0] = key;
     else if (f_diag && j == i) fkeys[f_first ? 1 : 0] = key;
     else keys[j - ((f_first && j > 0) ? 1 : 0)] = key;
@@ -186,6 +224,11 @@ hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.total_qblocks, (unsigned)a.hkv);
   hipLaunchKernelGGL(mask_pool_kernel, grid, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // groups of kScoreGroup blocks per sequence: at most total_qblocks / kScoreGroup + num_seqs
+  const dim3 sgrid((unsigned)(a.total_qblocks / kScoreGroup + a.num_seqs), (unsigned)a.hkv);
+  hipLaunchKernelGGL(mask_score_kernel, sgrid, dim3(256), 0, stream, a);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   // sort keys in LDS sized for the longest row (fewer workgroups per CU otherwise)
   int cap = 1;

@@ -42,9 +42,10 @@ struct BuilderArgs {
   const int32_t* cu_qblocks;
   int32_t* order_mask;
   int32_t* mask_len;
-  float* scores;  // nullable
-  float* qbar;    // workspace [total_qblocks, hkv, 128]
-  float* kbar;    // workspace [total_qblocks, hkv, 128]
+  float* scores;      // nullable (the caller's proxy_scores)
+  float* qbar;        // workspace [total_qblocks, hkv, 128]
+  float* kbar;        // workspace [total_qblocks, hkv, 128]
+  float* score_rows;  // [total_qblocks, hkv, max_pages]: scores, or workspace when scores is null
   int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
   float budget1;
