@@ -160,7 +160,10 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims,
  */
 int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t flags);
 
-/* Workspace bytes cosa_build_order_mask needs (pooled proxies). Host-only. */
+/* Workspace bytes cosa_build_order_mask needs: the fp32 pooled query and key
+ * proxies [total_qblocks, Hkv, 128] each and the fp32 score rows
+ * [total_qblocks, Hkv, max_pages_per_seq] (used when proxy_scores is NULL),
+ * each region padded to 256 bytes.  Host-only. */
 size_t cosa_build_order_mask_workspace_bytes(const cosa_osk_dims_t* dims);
 
 /*
