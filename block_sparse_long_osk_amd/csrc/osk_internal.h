@@ -27,7 +27,7 @@ struct PrefillArgs {
   uint8_t* decisions;
   float* margins;
   int32_t* sched;        // workspace: query-block visit order, [total_qblocks]
-  int32_t* error_count;  // workspace: workgroups whose bounded inter-wave waits aborted (0 when healthy)
+  int32_t* error_count;  // workspace health word (zeroed by the schedule kernel; 0 after every call)
   int64_t q_st, q_sh, o_st, o_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
   float sm_scale;

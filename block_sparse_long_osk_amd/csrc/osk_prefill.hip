@@ -23,10 +23,12 @@
 //   ds_read_b64_tr_b16 (transposing LDS read);
 // * K and V page tiles are gathered with global_load_lds_dwordx4 (direct to LDS,
 //   no VGPR staging) into a ring of kRing page slots; every wave gathers its
-//   share of each page kRing-1 visits ahead.  LDS counters say when a slot's
-//   page has landed (ready) and when every wave is done with it (used), so the
-//   heads of a group are not held in lock step by a per-visit barrier: a head
-//   that skips a page runs ahead of one that computes it;
+//   share of each page kRing-1 visits ahead;
+// * one workgroup barrier per visit, between a page's key side (S^T, row max,
+//   partial vote) and its value side, is the only inter-wave synchronisation: it
+//   publishes both halves' vote margins, certifies that every wave is done with
+//   the previous page (so its slot can be refilled) and, with each wave's wait
+//   for its own gathers before it, that the next page is resident;
 // * the visit list of a unit (mask row -> validity -> page table -> physical
 //   page, first occurrence of a repeated id only) is resolved in LDS windows of
 //   512 entries before the visits, so the hot loop does no dependent global loads;
@@ -54,7 +56,6 @@ constexpr int kTileBytes = kPage * kHeadDim * 2;  // one K or V page of one KV h
 constexpr int kPageBytes = 2 * kTileBytes;        // K then V
 constexpr int kWindow = 512;                      // mask entries resolved per window
 constexpr int kRing = 4;                          // page slots in flight per workgroup
-constexpr int kSpinLimit = 1 << 22;               // bound of every inter-wave wait
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kRebase = 8.f;  // log2 headroom of the lazily moved exponent base
@@ -120,28 +121,11 @@ __device__ __forceinline__ void wait_pages_outstanding(int pages) {
   else wait_vmcnt<3 * PW>();
 }
 
-__device__ __forceinline__ int lds_load_acquire(int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Workgroup barrier for LDS hand-offs: this wave's LDS accesses complete first;
+// the page gathers (vmcnt) are left in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
-__device__ __forceinline__ void lds_add_release(int* p, int v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-// Bounded wait until *ctr >= target.  Every wave of the workgroup is resident,
-// and each counter is advanced by waves that never wait on a later visit, so
-// the wait ends; the bound turns a broken protocol into an abort, never a hang.
-// The counter is polled back to back (one LDS round trip per poll); the abort
-// flag is checked every 64 polls and the wave sleeps between polls only once a
-// wait has lasted 256 polls.
-__device__ __forceinline__ bool wait_at_least(int* ctr, int target, int* abort_flag) {
-  for (int it = 0; it < kSpinLimit; ++it) {
-    if (__builtin_amdgcn_readfirstlane(lds_load_acquire(ctr)) >= target) return true;
-    if ((it & 63) == 63 && __builtin_amdgcn_readfirstlane(lds_load_acquire(abort_flag)) != 0) return false;
-    if (it >= 256) __builtin_amdgcn_s_sleep(1);
-  }
-  __hip_atomic_store(abort_flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return false;
-}
-
 // XOR swizzle of the 16-byte granule index inside a 256-byte K row (t = key row):
 // the 32 lanes of an MFMA A-operand read hit 16 distinct granules per 16 rows.
 __device__ __forceinline__ int swz_k(int t, int granule) { return granule ^ (t & 15); }
@@ -599,15 +583,16 @@ __device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
 }
 
 // ---------------------------------------------------------------------------
-// ring kernel: 1 or 2 q heads per workgroup (GQA groups of 1, 2, 3, 5, ...)
+// ring kernel: HW = 4, 2 or 1 q heads of one KV head's group per workgroup
 // ---------------------------------------------------------------------------
 // Two waves per head (32 rows each).  K and V page tiles share one ring of kRing
 // page slots; every wave gathers its share of each page kRing-1 visits ahead.
-// LDS counters say when a slot's page has landed (ready) and when every wave is
-// done with it (used), so a head that skips a page runs ahead of one that
-// computes it.  The two halves of a head combine their partial vote margins
-// through LDS.  Every inter-wave wait is bounded: a wait that runs out sets the
-// workgroup's abort flag and the workgroup is counted in the health word.
+// Visit v: S^T of page v and the 32-row partial vote margin (written to LDS);
+// this wave's wait for its share of page v+1; a workgroup barrier; then the
+// gather of page v+3 into the slot of page v-1 (every wave finished page v-1
+// before the barrier), the block vote from both halves' margins, and the value
+// side of page v unless it is skipped.  Every wave runs the same number of
+// barriers (the visit count is workgroup-uniform), so no wait can hang.
 template <int HW>
 __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const PrefillArgs a, int heads_per_group,
                                                                     int nsub) {
@@ -618,11 +603,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
   __shared__ WindowLds wlds;
   __shared__ uint8_t dec_lds[HW][kWindow];
   __shared__ float mar_lds[HW][kWindow];
-  __shared__ int ready_ctr[kRing];
-  __shared__ int used_ctr[kRing];
-  __shared__ int vote_seq[HW][2][2];
   __shared__ float vote_val[HW][2][2];
-  __shared__ int s_abort;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
@@ -653,7 +634,6 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     for (int e = 0; e < 16; ++e) o[nt][e] = 0.f;
 
   for (int x = threadIdx.x; x < (u.n_pages + 31) / 32; x += NT) wlds.seen_bits[x] = 0u;
-  if (threadIdx.x == 0) s_abort = 0;
 
   const int32_t* mrow = a.order_mask + ((int64_t)u.qb * a.hkv + u.g) * a.max_mask_len;
   const uint16_t* kbase = a.k + (int64_t)u.g * a.kv_sh;
@@ -665,8 +645,6 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     const int wl = min(kWindow, u.len - k0);
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
-    if (threadIdx.x < kRing) { ready_ctr[threadIdx.x] = 0; used_ctr[threadIdx.x] = 0; }
-    if (threadIdx.x < 4 * HW) (&vote_seq[0][0][0])[threadIdx.x] = 0;
     const int nv = resolve_window<NT>(a, u, mrow, k0, wl, wlds, wave, lane);
     auto gather = [&](int p) {
       const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]);
@@ -677,31 +655,21 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       tg.issue(vbase + off, slot + kTileBytes, valid_rows, true, wave, lane);
     };
 
-    // ---- ring prologue: gather pages 0 .. kRing-2, announce 0 .. kRing-3
+    // ---- prologue: gather pages 0 .. kRing-2; page 0 resident before the first QK
     const int pro = min(kRing - 1, nv);
     for (int p = 0; p < pro; ++p) gather(p);
-    for (int p = 0; p < min(kRing - 2, nv); ++p) {
-      wait_pages_outstanding<PW>(pro - 1 - p);
-      if (lane == 0) lds_add_release(&ready_ctr[p % kRing], 1);
+    if (nv > 0) {
+      wait_pages_outstanding<PW>(pro - 1);
+      lds_barrier();
     }
 
     for (int v = 0; v < nv; ++v) {
       const int slot = v % kRing;
-      // ---- keep kRing-1 pages in flight: gather page v+kRing-1 once every wave is done
-      //      with the page that held its slot, then announce page v+kRing-2
-      const int un = v + kRing - 1;
-      const int issued = min(un, nv - 1);
-      if (un < nv) {
-        if (!wait_at_least(&used_ctr[un % kRing], NW * (un / kRing), &s_abort)) break;
-        gather(un);
-      }
-      const int sgn = v + kRing - 2;
-      if (sgn < nv) {
-        wait_pages_outstanding<PW>(issued - sgn);
-        if (lane == 0) lds_add_release(&ready_ctr[sgn % kRing], 1);
-      }
-      // ---- page v resident in its slot (every wave's share has landed)
-      if (!wait_at_least(&ready_ctr[slot], NW * (v / kRing + 1), &s_abort)) break;
+      // page v+3's table entries, read ahead of the QK so the gather after the barrier
+      // does not wait on LDS (index clamped inside the window when there is no such page)
+      const int pg = min(v + kRing - 1, kWindow - 1);
+      const int pg_j = wlds.vis_j[pg];
+      const int pg_phys = wlds.vis_phys[pg];
       const int j = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
       const uint32_t kb = ring_addr + (uint32_t)slot * kPageBytes;
       const uint32_t vb = kb + kTileBytes;
@@ -713,20 +681,24 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       const float mnew2 = fmaxf(m2, mloc2);
       const float dd = (row_ok && mloc2 != -INFINITY) ? (mloc2 - mnew2) : -INFINITY;
       const float my_margin = max_lanes32(dd);
-      // exchange the 32-row partial margin with the other half of this head (needed
-      // only when pages can be skipped or the decisions are logged)
       const bool vote = skip_on || logging;
       const int par = v & 1;
-      if (vote && lane == 0) {
-        vote_val[hl][half][par] = my_margin;
-        __hip_atomic_store(&vote_seq[hl][half][par], v + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (vote && lane == 0) vote_val[hl][half][par] = my_margin;
+      // this wave's share of page v+1 has landed (page v+2's may still be in flight)
+      if (v + 1 < nv) wait_pages_outstanding<PW>(v + 2 < nv ? 1 : 0);
+      // one barrier per visit: past it, every wave has finished page v-1 (its slot is
+      // free), page v+1 is resident, and both halves' margins for page v are visible
+      lds_barrier();
+      const float partner = vote ? vote_val[hl][half ^ 1][par] : -INFINITY;
+      if (v + kRing - 1 < nv) {
+        const int jp = __builtin_amdgcn_readfirstlane(pg_j);
+        const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(pg_phys) * a.kv_sp;
+        const uint32_t gslot = ring_addr + (uint32_t)((v + kRing - 1) % kRing) * kPageBytes;
+        const int valid_rows = u.L - jp * kPage;
+        tg.issue(kbase + off, gslot, valid_rows, false, wave, lane);
+        tg.issue(vbase + off, gslot + kTileBytes, valid_rows, true, wave, lane);
       }
-      float margin2 = my_margin;
-      if (vote) {
-        if (!wait_at_least(&vote_seq[hl][half ^ 1][par], v + 1, &s_abort)) break;
-        margin2 = fmaxf(my_margin,
-                        __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vote_val[hl][half ^ 1][par]))));
-      }
+      const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(partner))));
       const bool skip = skip_on && (margin2 < tau2);
       if (logging && half == 0 && lane == 0) {
         dec_lds[hl][wlds.vis_k[v] - k0] = skip ? 1 : 0;
@@ -739,18 +711,13 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
         l2 += permlane32_sum(probs_tile(acc, scale_log2, b2, pb));
         pv_tile(vb, pb, lane, o);
       }
-      // every LDS read of this slot has returned (the release waits for the wave's
-      // outstanding LDS reads before the count moves)
-      if (lane == 0) lds_add_release(&used_ctr[slot], 1);
     }
     wait_vmcnt<0>();  // no page gather may still be writing LDS past this point
     __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
     if (logging && half == 0) flush_log(a, u, k0, wl, dec_lds[hl], mar_lds[hl], lane);
-    if (s_abort != 0) break;
     __syncthreads();
   }
   if (logging && half == 0) fill_log_tail(a, u, lane);
-  if (threadIdx.x == 0 && s_abort != 0) atomicAdd(a.error_count, 1);
   store_output(a, u, o, l2, b2, r_blk, row_ok, lane);
 }
 

@@ -137,9 +137,11 @@ cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_
  *             margins without decisions is COSA_ERR_INVALID_ARG).
  *   workspace device scratch of >= cosa_osk_workspace_bytes(dims) bytes, 16-byte
  *             aligned; its contents are overwritten.  After the call completes, the
- *             int32 at byte offset cosa_osk_workspace_bytes(dims) - 256 holds the
- *             number of workgroups whose bounded inter-wave waits gave up (0 in every
- *             healthy run; nonzero means the output of those blocks is not valid).
+ *             int32 at byte offset cosa_osk_workspace_bytes(dims) - 256 is a health
+ *             word: the number of workgroups that could not complete their visits
+ *             (nonzero would mean the output of those blocks is not valid).  The
+ *             kernels synchronise their waves with workgroup barriers only, so it
+ *             is 0 after every call; it is kept for callers that check it.
  * Numerics: fp32 accumulation of bf16 products for Q K^T, fp32 running max/sum,
  * probabilities rounded to bf16 for the P V product, fp32 output accumulator,
  * bf16 output.
