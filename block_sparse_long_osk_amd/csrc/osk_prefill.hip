@@ -22,8 +22,7 @@
 //   the B operand (bf16); V^T comes from the row-major V tile through
 //   ds_read_b64_tr_b16 (transposing LDS read);
 // * K and V page tiles are gathered with global_load_lds_dwordx4 (direct to LDS,
-//   no VGPR staging) into a ring of kRing page slots; every wave gathers its
-//   share of each page kRing-1 visits ahead;
+//   no VGPR staging) into a ring of kRing page slots, kRing-1 visits ahead;
 // * one workgroup barrier per visit, between a page's key side (S^T, row max,
 //   partial vote) and its value side, is the only inter-wave synchronisation: it
 //   publishes both halves' vote margins, certifies that every wave is done with
@@ -586,7 +585,10 @@ __device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
 // ring kernel: HW = 4, 2 or 1 q heads of one KV head's group per workgroup
 // ---------------------------------------------------------------------------
 // Two waves per head (32 rows each).  K and V page tiles share one ring of kRing
-// page slots; every wave gathers its share of each page kRing-1 visits ahead.
+// page slots; each page is gathered kRing-1 visits ahead by waves 0 .. GW-1 (with
+// eight waves, one per SIMD: the gather instructions of a page queue at the CU's
+// load path for ~500 cycles, and meanwhile the other wave of each SIMD runs its
+// value side alone, which staggers the two).
 // Visit v: S^T of page v and the 32-row partial vote margin (written to LDS);
 // this wave's wait for its share of page v+1; a workgroup barrier; then the
 // gather of page v+3 into the slot of page v-1 (every wave finished page v-1
@@ -598,7 +600,8 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
                                                                     int nsub) {
   constexpr int NW = 2 * HW;   // waves
   constexpr int NT = 64 * NW;  // threads
-  constexpr int PW = 32 / NW;  // page-gather instructions per wave per page
+  constexpr int GW = NW >= 4 ? NW / 2 : NW;  // waves that gather pages (waves 0 .. GW-1)
+  constexpr int PW = 32 / GW;                 // page-gather instructions per gathering wave per page
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
   __shared__ WindowLds wlds;
   __shared__ uint8_t dec_lds[HW][kWindow];
@@ -638,8 +641,9 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
   const int32_t* mrow = a.order_mask + ((int64_t)u.qb * a.hkv + u.g) * a.max_mask_len;
   const uint16_t* kbase = a.k + (int64_t)u.g * a.kv_sh;
   const uint16_t* vbase = a.v + (int64_t)u.g * a.kv_sh;
-  TileGather<NW> tg;
-  tg.init(a.kv_st, wave, lane);
+  const bool gatherer = wave < GW;
+  TileGather<GW> tg;
+  tg.init(a.kv_st, gatherer ? wave : 0, lane);
 
   for (int k0 = 0; k0 < u.len; k0 += kWindow) {
     const int wl = min(kWindow, u.len - k0);
@@ -651,8 +655,10 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(wlds.vis_phys[p]) * a.kv_sp;
       const uint32_t slot = ring_addr + (uint32_t)(p % kRing) * kPageBytes;
       const int valid_rows = u.L - jp * kPage;
-      tg.issue(kbase + off, slot, valid_rows, false, wave, lane);
-      tg.issue(vbase + off, slot + kTileBytes, valid_rows, true, wave, lane);
+      if (gatherer) {
+        tg.issue(kbase + off, slot, valid_rows, false, wave, lane);
+        tg.issue(vbase + off, slot + kTileBytes, valid_rows, true, wave, lane);
+      }
     };
 
     // ---- prologue: gather pages 0 .. kRing-2; page 0 resident before the first QK
@@ -690,7 +696,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       // free), page v+1 is resident, and both halves' margins for page v are visible
       lds_barrier();
       const float partner = vote ? vote_val[hl][half ^ 1][par] : -INFINITY;
-      if (v + kRing - 1 < nv) {
+      if (gatherer && v + kRing - 1 < nv) {
         const int jp = __builtin_amdgcn_readfirstlane(pg_j);
         const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(pg_phys) * a.kv_sp;
         const uint32_t gslot = ring_addr + (uint32_t)((v + kRing - 1) % kRing) * kPageBytes;
