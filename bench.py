@@ -61,6 +61,48 @@ def time_calls(fn, steps, warmup):
     return per, wall
 
 
+def calibrate():
+    """Attainable bf16 MFMA rate (independent 32x32x16 MFMA chains on every SIMD) and
+    HBM streaming-read rate (2 GiB, 16-byte loads) on this device, from the
+    measurement-only kernels of libcosa_calib.so, timed with events."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_sparse_long_osk_amd", "libcosa_calib.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_long_osk_amd.build`")
+    L = ctypes.CDLL(path)
+    L.cosa_calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    L.cosa_calib_mfma_bf16.restype = ctypes.c_int32
+    L.cosa_calib_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.cosa_calib_mfma_bf16_flop.restype = ctypes.c_double
+    L.cosa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    L.cosa_calib_read.restype = ctypes.c_int32
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nwg, iters = 256 * 8, 4096
+    out = torch.empty(nwg * 4, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        if L.cosa_calib_mfma_bf16(ctypes.c_void_p(out.data_ptr()), nwg, iters, stream) != 0:
+            raise RuntimeError("cosa_calib_mfma_bf16 failed")
+    per, _ = time_calls(mfma, 5, 2)
+    mfma_tflops = L.cosa_calib_mfma_bf16_flop(nwg, iters) / (statistics.median(per) * 1e-3) / 1e12
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rwg = 256 * 16
+    rout = torch.empty(rwg, dtype=torch.int32, device="cuda")
+
+    def read():
+        if L.cosa_calib_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(rout.data_ptr()), rwg,
+                             stream) != 0:
+            raise RuntimeError("cosa_calib_read failed")
+    per, _ = time_calls(read, 5, 2)
+    read_gbs = nbytes / (statistics.median(per) * 1e-3) / 1e9
+    del buf, rout, out
+    return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": read_gbs,
+            "how": "independent v_mfma_f32_32x32x16_bf16 chains, 2048 workgroups x 4 waves; "
+                   "2 GiB streaming read with 16-byte loads (libcosa_calib.so)"}
+
+
 def pct(xs, p):
     xs = sorted(xs)
     k = (len(xs) - 1) * p
@@ -237,6 +279,12 @@ def main():
                  "visited_q_head_pages": d_visited, "algorithmic_tflop": d_flop / 1e12}
         del douts, dom, dml
 
+    # ---- attainable rates on this device (measurement-only kernels)
+    print(f"[bench] calibrating MFMA and HBM rates", file=sys.stderr, flush=True)
+    attain = calibrate()
+    if dense:
+        dense["frac_of_attainable"] = dense["tflops"] / attain["mfma_bf16_tflops"]
+
     # ---- roofline of the dominant kernel
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -247,7 +295,8 @@ def main():
     kv_bytes = 2 * 64 * 128 * 2 * (visited // (db.num_q_heads // db.num_kv_heads))
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": "osk_prefill_kernel<4> (+ schedule kernel, <0.1% of the call)",
+                "frac_of_attainable": tflops / attain["mfma_bf16_tflops"],
+                "kernel": "osk_prefill_ring_kernel<4> (+ schedule kernel, 0.3% of the call)",
                 "algorithmic_flop_per_launch": flop,
                 "kv_gather_gbs": kv_bytes / (med * 1e-3) / 1e9,
                 "kv_gather_frac_of_hbm": kv_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -273,7 +322,7 @@ def main():
         "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
         "dense": dense, "mask_builder_ms": statistics.median(builder_ms),
         "osk_plus_builder_ms": med + statistics.median(builder_ms),
-        "roofline": roofline, "cpu_baseline": cpu, "aborted_workgroups": aborts,
+        "roofline": roofline, "attainable": attain, "cpu_baseline": cpu, "aborted_workgroups": aborts,
     }
     print(json.dumps(rec), flush=True)
 

@@ -13,6 +13,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libcosa_osk.so")
 SOURCES = ["osk_prefill.hip", "mask_builder.hip", "api.cpp"]
+# measurement-only microbenchmarks (attainable MFMA and HBM read rates), a library of their own
+CALIB_LIB_PATH = os.path.join(PKG, "libcosa_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 
 def hipcc() -> str:
@@ -23,8 +26,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library; returns its path."""
-    tmp = LIB_PATH + ".tmp"
+    """Compile every source for gfx950 and link both shared libraries; returns the
+    attention library's path."""
+    _link(SOURCES, LIB_PATH, verbose)
+    _link(CALIB_SOURCES, CALIB_LIB_PATH, verbose)
+    return LIB_PATH
+
+
+def _link(sources, lib_path, verbose):
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms stay off in all device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,7 +42,7 @@ def build(verbose: bool = False) -> str:
            # serve as spill space instead of holding S and O behind copy instructions
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,8 +53,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
 
 
 if __name__ == "__main__":

@@ -17,25 +17,54 @@ OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH), reason="library not built")
 
 
-def declared_functions():
+CALIB_LIB_PATH = os.path.join(os.path.dirname(binding.LIB_PATH), "libcosa_calib.so")
+
+
+def declared_functions(headers):
     names = []
-    for fn in os.listdir(os.path.join(ROOT, "include")):
-        if fn.endswith(".h"):
-            text = open(os.path.join(ROOT, "include", fn)).read()
-            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names += re.findall(r"\b(cosa_[a-z0-9_]+)\s*\(", text)
+    for fn in headers:
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(cosa_[a-z0-9_]+)\s*\(", text)
     return sorted(set(names))
+
+
+def test_every_header_is_checked():
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        ["cosa_calib.h", "cosa_osk.h"]
 
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(binding.LIB_PATH)
-    names = declared_functions()
+    names = declared_functions(["cosa_osk.h"])
     assert len(names) >= 9
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
     assert binding.cosa_abi_version() == 1
     assert binding.cosa_status_string(-3).startswith("workspace")
+
+
+@pytest.mark.skipif(not os.path.exists(CALIB_LIB_PATH), reason="calibration library not built")
+def test_calibration_library_exports_and_host_checks():
+    lib = ctypes.CDLL(CALIB_LIB_PATH)
+    names = declared_functions(["cosa_calib.h"])
+    assert names == ["cosa_calib_mfma_bf16", "cosa_calib_mfma_bf16_flop", "cosa_calib_read"]
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.cosa_calib_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.cosa_calib_mfma_bf16_flop.restype = ctypes.c_double
+    # 8 MFMAs of 32x32x16 multiply-adds per round, 4 waves per workgroup
+    assert lib.cosa_calib_mfma_bf16_flop(3, 5) == 2 * 32 * 32 * 16 * 8 * 5 * 4 * 3
+    # argument errors are caught on the host before any launch
+    lib.cosa_calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.cosa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    assert lib.cosa_calib_mfma_bf16(None, 1, 1, None) == -1
+    assert lib.cosa_calib_mfma_bf16(ctypes.c_void_p(16), 0, 1, None) == -1
+    assert lib.cosa_calib_read(None, 16, ctypes.c_void_p(16), 1, None) == -1
+    assert lib.cosa_calib_read(ctypes.c_void_p(16), 17, ctypes.c_void_p(16), 1, None) == -1
+    assert lib.cosa_calib_read(ctypes.c_void_p(24), 16, ctypes.c_void_p(16), 1, None) == -1
 
 
 def good_dims(**kw):
