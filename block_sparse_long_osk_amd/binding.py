@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcosa_osk
 COSA_OK = 0
 COSA_DECISION_COMPUTED, COSA_DECISION_SKIPPED, COSA_DECISION_NOT_VISITED = 0, 1, 2
 COSA_FORCE_FIRST, COSA_FORCE_DIAG = 1, 2
+COSA_KAP_FRACTION, COSA_KAP_TOP_P = 0, 1
 PAGE_SIZE, HEAD_DIM = 64, 128
 
 
@@ -67,6 +68,13 @@ def lib():
         L.cosa_build_order_mask.restype = ctypes.c_int
         L.cosa_build_order_mask.argtypes = [D, P, P, P, P, P, ctypes.c_float, ctypes.c_uint32, P, P, P, P,
                                             ctypes.c_size_t, P]
+        L.cosa_kap_mask_width.restype = ctypes.c_int32
+        L.cosa_kap_mask_width.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_float]
+        L.cosa_build_kap_mask_workspace_bytes.restype = ctypes.c_size_t
+        L.cosa_build_kap_mask_workspace_bytes.argtypes = [D]
+        L.cosa_build_kap_mask.restype = ctypes.c_int
+        L.cosa_build_kap_mask.argtypes = [D, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P, P, P,
+                                          P, P, ctypes.c_size_t, P]
         L.cosa_validate_order_mask.restype = ctypes.c_int
         L.cosa_validate_order_mask.argtypes = [D, P, P, P, P, P, P, P]
         _lib = L
@@ -75,7 +83,8 @@ def lib():
 
 EXPORTED = ["cosa_abi_version", "cosa_status_string", "cosa_osk_workspace_bytes", "cosa_osk_check_args",
             "cosa_osk_prefill", "cosa_order_mask_width", "cosa_build_order_mask_workspace_bytes",
-            "cosa_build_order_mask", "cosa_validate_order_mask"]
+            "cosa_build_order_mask", "cosa_validate_order_mask", "cosa_kap_mask_width",
+            "cosa_build_kap_mask_workspace_bytes", "cosa_build_kap_mask"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -166,6 +175,28 @@ def cosa_build_order_mask(dims: CosaOskDims, q, k_pool, page_table, cu_seqlens, 
                                      _ptr(proxy_scores), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "cosa_build_order_mask")
+
+
+def cosa_kap_mask_width(max_pages_per_seq: int, mode: int, budget: float) -> int:
+    return lib().cosa_kap_mask_width(int(max_pages_per_seq), int(mode), float(budget))
+
+
+def cosa_build_kap_mask_workspace_bytes(dims: CosaOskDims) -> int:
+    return lib().cosa_build_kap_mask_workspace_bytes(ctypes.byref(dims))
+
+
+def cosa_build_kap_mask(dims: CosaOskDims, q, k_pool, page_table, cu_seqlens, cu_qblocks, stride: int, mode: int,
+                        budget: float, order_mask, mask_len, kap_scores=None, hrm_flags=None, workspace=None,
+                        stream=None):
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(cosa_build_kap_mask_workspace_bytes(dims), 256), dtype=torch.uint8,
+                                device=q.device)
+    st = lib().cosa_build_kap_mask(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(page_table), _ptr(cu_seqlens),
+                                   _ptr(cu_qblocks), int(stride), int(mode), float(budget), _ptr(order_mask),
+                                   _ptr(mask_len), _ptr(kap_scores), _ptr(hrm_flags), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "cosa_build_kap_mask")
 
 
 def cosa_validate_order_mask(dims: CosaOskDims, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libcosa_osk.so")
-SOURCES = ["osk_prefill.hip", "mask_builder.hip", "api.cpp"]
+SOURCES = ["osk_prefill.hip", "mask_builder.hip", "kap.hip", "api.cpp"]
 # measurement-only microbenchmarks (attainable MFMA and HBM read rates), a library of their own
 CALIB_LIB_PATH = os.path.join(PKG, "libcosa_calib.so")
 CALIB_SOURCES = ["calib.hip"]

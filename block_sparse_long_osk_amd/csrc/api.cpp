@@ -2,6 +2,8 @@
 // sizing, and kernel launches on the caller's stream.  Declarations and the
 // contract of every function are in include/cosa_osk.h.
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "cosa_osk.h"
@@ -208,6 +210,83 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   a.budget1 = budget1;
   a.flags = flags;
   return cosa_osk::launch_build_order_mask(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
+}
+
+int32_t cosa_kap_mask_width(int32_t max_pages_per_seq, int32_t mode, float budget) {
+  if (max_pages_per_seq < 1) return -1;
+  if (mode == COSA_KAP_TOP_P) return max_pages_per_seq;
+  if (mode != COSA_KAP_FRACTION) return -1;
+  const int w = (int)ceil((double)budget * (double)max_pages_per_seq - 1e-3);
+  return std::max(1, std::min(max_pages_per_seq, w));
+}
+
+// KAP workspace: fp32 score rows then uint8 flag rows, [total_qblocks, Hkv, max_pages] each
+static size_t kap_score_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(d->max_pages_per_seq, 0) *
+                      sizeof(float) + 1);
+}
+static size_t kap_flag_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(d->max_pages_per_seq, 0) + 1);
+}
+
+size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims) {
+  if (dims == nullptr || dims->total_qblocks < 0 || dims->num_kv_heads < 1) return 0;
+  return kap_score_bytes(dims) + kap_flag_bytes(dims);
+}
+
+cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                  const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                                  int32_t stride, int32_t mode, float budget, int32_t* order_mask,
+                                  int32_t* mask_len, float* kap_scores, uint8_t* hrm_flags, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  if (dims->max_pages_per_seq > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
+  if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
+      order_mask == nullptr || mask_len == nullptr)
+    return COSA_ERR_INVALID_ARG;
+  if (mode != COSA_KAP_FRACTION && mode != COSA_KAP_TOP_P) return COSA_ERR_INVALID_ARG;
+  if (mode == COSA_KAP_FRACTION ? !(budget > 0.f && budget <= 1.f) : !(budget >= 0.f && budget <= 1.f))
+    return COSA_ERR_INVALID_ARG;
+  if (stride != 8 && stride != 16) return COSA_ERR_UNSUPPORTED;
+  const int G = dims->num_q_heads / dims->num_kv_heads;
+  // the sampled rows of a query block (all heads of the group) form a power-of-two group
+  // of at most 32 MFMA columns
+  const int rb = G * (cosa_osk::kPage / stride);
+  if (rb > 32 || (rb & (rb - 1)) != 0) return COSA_ERR_UNSUPPORTED;
+  if (dims->max_mask_len < cosa_kap_mask_width(dims->max_pages_per_seq, mode, budget)) return COSA_ERR_INVALID_ARG;
+  const size_t need = cosa_build_kap_mask_workspace_bytes(dims);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
+  cosa_osk::KapArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_pool);
+  a.page_table = page_table;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_qblocks = cu_qblocks;
+  a.order_mask = order_mask;
+  a.mask_len = mask_len;
+  a.scores_out = kap_scores;
+  a.flags_out = hrm_flags;
+  a.score_rows = kap_scores != nullptr ? kap_scores : static_cast<float*>(workspace);
+  a.flag_rows = hrm_flags != nullptr ? hrm_flags
+                                     : reinterpret_cast<uint8_t*>(static_cast<char*>(workspace) + kap_score_bytes(dims));
+  a.q_st = dims->q_stride_tok;
+  a.q_sh = dims->q_stride_head;
+  a.kv_sp = dims->kv_stride_page;
+  a.kv_sh = dims->kv_stride_head;
+  a.kv_st = dims->kv_stride_tok;
+  a.num_seqs = dims->num_seqs;
+  a.hq = dims->num_q_heads;
+  a.hkv = dims->num_kv_heads;
+  a.total_qblocks = dims->total_qblocks;
+  a.max_pages = dims->max_pages_per_seq;
+  a.num_phys = dims->num_phys_pages;
+  a.max_mask_len = dims->max_mask_len;
+  a.stride = stride;
+  a.mode = mode;
+  a.budget = budget;
+  a.sm_scale = resolved_scale(dims);
+  return cosa_osk::launch_build_kap_mask(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
 }
 
 cosa_status_t cosa_validate_order_mask(const cosa_osk_dims_t* dims, const int32_t* page_table,

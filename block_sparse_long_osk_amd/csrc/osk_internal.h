@@ -62,7 +62,26 @@ struct ValidateArgs {
   int32_t num_seqs, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
 };
 
+struct KapArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* page_table;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_qblocks;
+  int32_t* order_mask;
+  int32_t* mask_len;
+  float* scores_out;    // nullable: the caller's copy of the block scores
+  uint8_t* flags_out;   // nullable: the caller's copy of the HRM flags
+  float* score_rows;    // [total_qblocks, hkv, max_pages]: scores_out, or workspace
+  uint8_t* flag_rows;   // [total_qblocks, hkv, max_pages]: flags_out, or workspace
+  int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
+  int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
+  int32_t stride, mode;
+  float budget, sm_scale;
+};
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_build_kap_mask(const KapArgs& a, hipStream_t stream);
 hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 

@@ -124,6 +124,24 @@ def build_mask(db: DeviceBatch, budget1: float, flags: int = COSA_FORCE_FIRST | 
     return (om, ml, sc) if scores else (om, ml)
 
 
+def build_kap_mask(db: DeviceBatch, stride: int, mode: int, budget: float, width: Optional[int] = None,
+                   outputs: bool = False, workspace=None, stream=None):
+    """cosa_build_kap_mask on the device batch; returns (order_mask, mask_len[, scores, flags])."""
+    import torch
+    max_pages = db.page_table.shape[1]
+    if width is None:
+        width = binding.cosa_kap_mask_width(max_pages, mode, budget)
+    dims = db.dims(width)
+    dev = db.q.device
+    om = torch.empty((db.total_qblocks, db.num_kv_heads, width), dtype=torch.int32, device=dev)
+    ml = torch.empty((db.total_qblocks, db.num_kv_heads), dtype=torch.int32, device=dev)
+    sc = torch.empty((db.total_qblocks, db.num_kv_heads, max_pages), dtype=torch.float32, device=dev) if outputs else None
+    fl = torch.empty((db.total_qblocks, db.num_kv_heads, max_pages), dtype=torch.uint8, device=dev) if outputs else None
+    binding.cosa_build_kap_mask(dims, db.q, db.k_pool, db.page_table, db.cu_seqlens, db.cu_qblocks, stride, mode,
+                                budget, om, ml, kap_scores=sc, hrm_flags=fl, workspace=workspace, stream=stream)
+    return (om, ml, sc, fl) if outputs else (om, ml)
+
+
 def validate_mask(db: DeviceBatch, order_mask, mask_len, stream=None) -> np.ndarray:
     """cosa_validate_order_mask; returns the 5 counters on the host."""
     import torch

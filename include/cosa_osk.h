@@ -191,6 +191,50 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
                                     int32_t* order_mask, int32_t* mask_len, float* proxy_scores,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Stage-1 selection modes of cosa_build_kap_mask. */
+#define COSA_KAP_FRACTION 0 /* K_i = ceil(budget * (i + 1) - 1e-3), at least 1            */
+#define COSA_KAP_TOP_P 1    /* smallest K_i whose leading scores reach budget of the total */
+
+/* Row width a KAP mask needs: ceil(budget * max_pages - 1e-3) clamped to
+ * [1, max_pages] for COSA_KAP_FRACTION, max_pages for COSA_KAP_TOP_P.  Host-only.
+ * Returns -1 for max_pages_per_seq < 1 or an unknown mode. */
+int32_t cosa_kap_mask_width(int32_t max_pages_per_seq, int32_t mode, float budget);
+
+/* Workspace bytes cosa_build_kap_mask needs: fp32 block scores and uint8 HRM flags
+ * [total_qblocks, Hkv, max_pages_per_seq] each, each region padded to 256 bytes
+ * (used where the caller passes no array of its own).  Host-only. */
+size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims);
+
+/*
+ * Kernel-aware proxy (KAP) computation-order mask (CoSA section 4.2, Eq. (8)-(14);
+ * Appendix C, Figure A and Algorithm A, pre-kernel proxy).  For every query block i
+ * of sequence s and KV head g:
+ *   Q~, K~ = every stride-th token of the sequence (token r*stride is sample r);
+ *   S^ = row-wise softmax of Q~ K~^T * sm_scale with sample c visible to sample r
+ *   iff c <= r (sm_scale = dims->sm_scale, 0 meaning 1/sqrt(128));
+ *   P[r, j] = max of S^[r, c] over the sampled keys of page-sized block j (0 if none
+ *   is visible); Pbar[r, j] = P[r, j] / max_j' P[r, j'];
+ *   score s_ij = sum of Pbar[r, j] over the block's sampled rows r of all G q heads
+ *   of the group; HRM flag h_ij = 1 if any of those rows has Pbar[r, j] = 1;
+ *   the causal candidates j <= i sorted HRM blocks first, then by score descending,
+ *   equal scores by block id ascending; the leading K_i of them (mode, budget:
+ *   COSA_KAP_FRACTION with budget in (0, 1], or COSA_KAP_TOP_P with budget = p in
+ *   [0, 1]) are the row, -1 after.
+ * order_mask [total_qblocks, Hkv, max_mask_len] and mask_len [total_qblocks, Hkv]
+ * are written; dims->max_mask_len must be >= cosa_kap_mask_width(...).
+ * kap_scores (nullable) fp32 and hrm_flags (nullable) uint8, both
+ * [total_qblocks, Hkv, max_pages_per_seq]: s_ij and h_ij for j <= i, NaN / 0 after.
+ * Supported: stride 8 or 16, and G * 64 / stride a power of two <= 32 (G = Hq / Hkv);
+ * max_pages_per_seq <= 8192; otherwise COSA_ERR_UNSUPPORTED.  The page-table entries
+ * of a sequence's pages must be valid physical pages.  k_pool uses the dims' KV
+ * strides.  Asynchronous on `stream`; the workspace is overwritten.
+ */
+cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                  const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                                  int32_t stride, int32_t mode, float budget, int32_t* order_mask,
+                                  int32_t* mask_len, float* kap_scores, uint8_t* hrm_flags, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Count malformed mask entries (PageWeaver notes section 2.1 conventions: such
  * entries add no interaction; the prefill treats them as not visited).

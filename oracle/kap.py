@@ -117,13 +117,16 @@ def mask_width(max_pages: int, mode: int, budget: float) -> int:
 
 
 def build_kap_mask(q, k_pool, page_table, cu_seqlens, num_kv_heads: int, stride: int, mode: int, budget: float,
-                   page_size: int = 64, width: Optional[int] = None, blocks: Optional[List[int]] = None):
+                   page_size: int = 64, width: Optional[int] = None, blocks: Optional[List[int]] = None,
+                   return_hmax: bool = False):
     """KAP mask of every (query block, KV head), or of the global query blocks listed.
 
     Returns order_mask [nqb, Hkv, width] int32 (-1 padded), mask_len [nqb, Hkv],
     scores [nqb, Hkv, max_pages] float64 (NaN past the causal candidates) and
     flags [nqb, Hkv, max_pages] uint8 (0 past them); with `blocks`, nqb = len(blocks)
-    in that order.
+    in that order.  With return_hmax, also the largest Pbar of each (block, key block)
+    over the group's sampled rows (the quantity Eq. (12) compares with 1; NaN past the
+    candidates).
     """
     if page_size % stride != 0:
         raise ValueError("the stride must divide the page size")
@@ -143,6 +146,7 @@ def build_kap_mask(q, k_pool, page_table, cu_seqlens, num_kv_heads: int, stride:
     ml = np.zeros((nqb, num_kv_heads), dtype=np.int32)
     sc = np.full((nqb, num_kv_heads, max_pages), np.nan)
     fl = np.zeros((nqb, num_kv_heads, max_pages), dtype=np.uint8)
+    hm = np.full((nqb, num_kv_heads, max_pages), np.nan)
     by_seq = {}
     for pos, qb in enumerate(want):
         sidx = int(np.searchsorted(starts, qb, side="right") - 1)
@@ -169,4 +173,7 @@ def build_kap_mask(q, k_pool, page_table, cu_seqlens, num_kv_heads: int, stride:
                 ml[pos, g] = k
                 sc[pos, g, : i + 1] = s_row
                 fl[pos, g, : i + 1] = h_row
+                hm[pos, g, : i + 1] = hmax
+    if return_hmax:
+        return om, ml, sc, fl, hm
     return om, ml, sc, fl

@@ -140,3 +140,34 @@ def test_builder_rejects_bad_arguments():
     assert call(dd=good_dims(max_mask_len=3)) == INVALID          # narrower than the mask needs
     assert call(dd=good_dims(max_mask_len=20), wsb=16) == WORKSPACE
     assert call(dd=good_dims(max_mask_len=20, max_pages_per_seq=9000, total_qblocks=64)) == UNSUPPORTED
+
+
+def test_kap_mask_width_matches_oracle():
+    from oracle import kap
+    for mode, b in [(0, 0.1), (0, 0.3), (0, 1.0), (1, 0.95), (1, 0.0)]:
+        for mp in (1, 3, 64, 2048, 8192):
+            assert binding.cosa_kap_mask_width(mp, mode, b) == kap.mask_width(mp, mode, b), (mode, b, mp)
+    assert binding.cosa_kap_mask_width(0, 0, 0.5) == -1
+    assert binding.cosa_kap_mask_width(64, 2, 0.5) == -1
+
+
+def test_kap_builder_rejects_bad_arguments():
+    L = binding.lib()
+    d = good_dims(max_mask_len=64)
+    fake = 0x10000
+    need = binding.cosa_build_kap_mask_workspace_bytes(d)
+    assert need >= 64 * 8 * 64 * 5
+    def call(dd=d, stride=16, mode=0, b=0.3, wsb=need, work=fake):
+        return L.cosa_build_kap_mask(ctypes.byref(dd), fake, fake, fake, fake, fake, stride, mode, b, fake, fake,
+                                     None, None, work, wsb, None)
+    assert call(mode=2) == INVALID
+    assert call(b=0.0) == INVALID                                   # a fixed fraction of zero keeps nothing
+    assert call(mode=1, b=1.5) == INVALID
+    assert call(stride=32) == UNSUPPORTED
+    assert call(stride=4) == UNSUPPORTED
+    assert call(dd=good_dims(num_q_heads=24, max_mask_len=64)) == UNSUPPORTED      # G = 3: 12 rows per block
+    assert call(dd=good_dims(num_q_heads=64, max_mask_len=64), stride=8) == UNSUPPORTED  # G = 8 at stride 8: 64 rows
+    assert call(dd=good_dims(max_mask_len=10)) == INVALID          # narrower than the mask needs
+    assert call(mode=1, dd=good_dims(max_mask_len=63)) == INVALID  # Top-p rows can hold every candidate
+    assert call(wsb=16) == WORKSPACE
+    assert call(dd=good_dims(max_mask_len=64, max_pages_per_seq=9000)) == UNSUPPORTED

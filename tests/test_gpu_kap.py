@@ -1,0 +1,139 @@
+"""Parity of the KAP mask builder (cosa_build_kap_mask, through the C ABI) with the
+fp64 KAP oracle (CoSA section 4.2, Eq. (8)-(14)), on an MI355X.
+
+The kernel's block scores must match the oracle's within fp32 rounding; its HRM flags
+must match except where two blocks hold a row's maximum within fp32 rounding of the
+logits; every mask row must be exactly the order the kernel's own scores and flags
+define (HRM first, score descending, id ascending), with the fixed-fraction length
+exact and the Top-p length equal to the oracle's or off by one only where the
+cumulative score sits within rounding of the threshold.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from block_sparse_long_osk_amd import inputs
+from oracle import kap
+from tests.parity_helpers import host_arrays
+
+pytestmark = pytest.mark.gpu
+
+FLAG_TIE = 1e-4   # a Pbar within this of 1 may be the row maximum on either side
+
+
+def log(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def rt():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_sparse_long_osk_amd import binding, runner
+    binding.lib()  # raises if the HIP library is missing: no fallback path exists
+    return runner
+
+
+def expected_row(s, h, n):
+    ids = np.arange(s.size)
+    return ids[np.lexsort((ids, -s.astype(np.float64), -h.astype(np.int64)))][:n]
+
+
+def check_kap(rt, name, batch, stride, mode, budget, blocks=None):
+    import torch
+    Hkv = batch.k_pool.shape[1]
+    db = rt.upload(batch)
+    om_d, ml_d, sc_d, fl_d = rt.build_kap_mask(db, stride, mode, budget, outputs=True)
+    torch.cuda.synchronize()
+    om_g, ml_g = om_d.cpu().numpy(), ml_d.cpu().numpy()
+    sc_g, fl_g = sc_d.cpu().numpy(), fl_d.cpu().numpy()
+    q, k, _ = host_arrays(batch)
+    nqb = om_g.shape[0]
+    want = list(range(nqb)) if blocks is None else list(blocks)
+    om_o, ml_o, sc_o, fl_o, hm_o = kap.build_kap_mask(q, k, batch.page_table, batch.cu_seqlens, Hkv, stride, mode,
+                                                      budget, width=om_g.shape[2], blocks=want, return_hmax=True)
+    starts = np.cumsum([0] + [-(-int(L) // 64) for L in np.diff(batch.cu_seqlens)])
+    stats = dict(units=0, flag_ties=0, len_ties=0, max_score_err=0.0)
+    for pos, qb in enumerate(want):
+        sidx = int(np.searchsorted(starts, qb, side="right") - 1)
+        i = qb - int(starts[sidx])
+        for g in range(Hkv):
+            stats["units"] += 1
+            so, sg = sc_o[pos, g, : i + 1], sc_g[qb, g, : i + 1]
+            np.testing.assert_allclose(sg, so, rtol=2e-3, atol=2e-3, err_msg=f"{name} scores qb {qb} g {g}")
+            stats["max_score_err"] = max(stats["max_score_err"], float(np.max(np.abs(sg - so))))
+            assert np.all(np.isnan(sc_g[qb, g, i + 1:])) and np.all(fl_g[qb, g, i + 1:] == 0)
+            fo, fg = fl_o[pos, g, : i + 1].astype(bool), fl_g[qb, g, : i + 1].astype(bool)
+            near = hm_o[pos, g, : i + 1] >= 1.0 - FLAG_TIE
+            diff = fo != fg
+            if diff.any():
+                # only near-maximal blocks may differ, and only in rows with two of them
+                assert np.all(near[diff]) and near.sum() >= 2, f"{name} flags qb {qb} g {g}: {np.flatnonzero(diff)}"
+                stats["flag_ties"] += int(diff.sum())
+            n = int(ml_g[qb, g])
+            row = om_g[qb, g]
+            assert np.all(row[n:] == -1)
+            assert list(row[:n]) == list(expected_row(sg, fg.astype(np.int64), n)), f"{name} order qb {qb} g {g}"
+            if mode == kap.MODE_FRACTION:
+                assert n == int(ml_o[pos, g])
+            elif n != int(ml_o[pos, g]):
+                order = expected_row(so, fo.astype(np.int64), i + 1)
+                cs = np.cumsum(so[order])
+                thr = np.float32(budget) * so.sum()
+                k = int(ml_o[pos, g])
+                assert abs(n - k) == 1, f"{name} top-p length qb {qb} g {g}: {n} vs {k}"
+                edge = cs[min(n, k) - 1]
+                assert abs(edge - thr) <= 1e-3 * max(1.0, thr), f"{name} top-p edge qb {qb} g {g}"
+                stats["len_ties"] += 1
+    assert stats["flag_ties"] <= max(2, stats["units"] // 100)
+    log(name, stats)
+    return stats
+
+
+SMALL = [
+    # name, seq_lens, hq, hkv, generator, pool, stride, mode, budget
+    ("gqa4_s16_frac", [64 * 37 + 13, 64 * 5], 8, 2, "structured", "shuffled", 16, kap.MODE_FRACTION, 0.3),
+    ("gqa4_s16_topp", [64 * 37 + 13, 64 * 5], 8, 2, "structured", "shuffled", 16, kap.MODE_TOP_P, 0.9),
+    ("gqa4_s8_frac", [64 * 20 + 40], 8, 2, "iid", "identity", 8, kap.MODE_FRACTION, 0.5),
+    ("gqa4_s8_topp", [64 * 20 + 40], 8, 2, "structured", "identity", 8, kap.MODE_TOP_P, 0.95),
+    ("mha_s16", [64 * 30 + 1], 2, 2, "iid", "shuffled", 16, kap.MODE_FRACTION, 0.2),
+    ("gqa2_s8", [64 * 9, 64 * 9 + 63, 17], 4, 2, "structured", "shuffled", 8, kap.MODE_TOP_P, 0.8),
+    ("gqa8_s16", [64 * 12 + 5], 16, 2, "structured", "identity", 16, kap.MODE_FRACTION, 0.25),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_kap_small(rt, case):
+    name, lens, hq, hkv, gen, pool, stride, mode, budget = case
+    log("case", name, lens, hq, hkv, gen, pool, stride, mode, budget)
+    wl = inputs.small_workload(name, lens, hq, hkv, generator=gen, seed=77, pool=pool)
+    check_kap(rt, name, inputs.generate(wl), stride, mode, budget)
+
+
+def test_kap_rejects_unsupported(rt):
+    import torch
+    from block_sparse_long_osk_amd import binding
+    wl = inputs.small_workload("rej", [64 * 3], 12, 4, generator="iid", seed=1, pool="identity")  # G = 3
+    db = rt.upload(inputs.generate(wl))
+    with pytest.raises(binding.CosaError):
+        rt.build_kap_mask(db, 16, kap.MODE_FRACTION, 0.5)
+    wl = inputs.small_workload("rej2", [64 * 3], 8, 2, generator="iid", seed=1, pool="identity")
+    db = rt.upload(inputs.generate(wl))
+    with pytest.raises(binding.CosaError):
+        rt.build_kap_mask(db, 32, kap.MODE_FRACTION, 0.5)         # stride 32: not supported
+    with pytest.raises(binding.CosaError):
+        rt.build_kap_mask(db, 16, 7, 0.5, width=8)                 # unknown mode
+    torch.cuda.synchronize()
+
+
+def test_kap_full_size_128k_sampled(rt):
+    wl = inputs.WORKLOADS["cfg4_128k_structured"]
+    batch = inputs.generate(wl)
+    rng = np.random.default_rng(5)
+    blocks = sorted(set([0, 1, 2047] + rng.choice(2048, 24, replace=False).tolist()))
+    log("cfg4 KAP sampled blocks", blocks)
+    check_kap(rt, "cfg4_kap_frac", batch, 16, kap.MODE_FRACTION, 0.1, blocks=blocks)
+    check_kap(rt, "cfg4_kap_topp", batch, 16, kap.MODE_TOP_P, 0.95, blocks=blocks[:12])
