@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TILE_FLOP = 2 * 64 * 64 * 128  # one 64x64x128 contraction
+KAP_STRIDE = 16
 KERNEL_SOURCES = ["block_sparse_long_osk_amd/csrc/osk_prefill.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "osk_prefill_cfg4_128k_traffic.json")
 
@@ -149,10 +150,11 @@ def cpu_baseline(batch, wl, delta, budget_s=15.0):
             "seconds": round(spent, 2)}
 
 
-def skip_sweep(args, wl, db, om, ml):
+def skip_sweep(args, wl, db, om, ml, mask_kind="proxy"):
     """Skip ratio and ms per call against Delta for two visit orders of the same page sets:
-    the proxy's (score descending) and ascending page id.  tau = ln(Delta / L) is swept over a
-    fixed grid; the pages' own Delta = 2000 is included."""
+    the mask's own order (the mean-pooled proxy's score-descending order, or KAP's
+    HRM-first order) and ascending page id.  tau = ln(Delta / L) is swept over a fixed
+    grid; the pages' own Delta = 2000 is included."""
     import numpy as np
     import torch
     from block_sparse_long_osk_amd import runner
@@ -163,7 +165,7 @@ def skip_sweep(args, wl, db, om, ml):
     for idx in np.ndindex(ml_h.shape):
         n = int(ml_h[idx])
         asc[idx][:n] = np.sort(asc[idx][:n])
-    orders = {"proxy": (om, ml), "ascending": runner.upload_mask(asc, ml_h)}
+    orders = {mask_kind: (om, ml), "ascending": runner.upload_mask(asc, ml_h)}
     L = max(wl.seq_lens)
     deltas = [("tau", float(L * np.exp(t)), t) for t in (-1.0, -0.5, -0.3, -0.2, -0.15, -0.1, -0.05, -0.02, 0.0)]
     deltas.append(("pages_delta", 2000.0, float(np.log(2000.0 / L))))
@@ -171,7 +173,8 @@ def skip_sweep(args, wl, db, om, ml):
     outs.lse = None
     ws = runner.workspace_for(db, width)
     for kind, delta, tau in deltas:
-        row = {"mode": "skip-sweep", "workload": wl.name, "delta": delta, "tau_at_longest_seq": tau, "kind": kind}
+        row = {"mode": "skip-sweep", "mask": mask_kind, "workload": wl.name, "delta": delta,
+               "tau_at_longest_seq": tau, "kind": kind}
         for name, (m, mlen) in orders.items():
             logged = runner.prefill(db, m, mlen, delta, log=True)
             torch.cuda.synchronize()
@@ -193,6 +196,9 @@ def main():
     ap.add_argument("--workload", default="cfg4_128k_structured")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--mask", choices=["proxy", "kap"], default="proxy",
+                    help="skip-sweep: sweep with the mean-pooled proxy masks or with KAP masks (stride 16, "
+                         "the workload's budget as the fixed fraction)")
     ap.add_argument("--mode", choices=["bench", "counters", "skip-sweep"], default="bench",
                     help="counters: a plain 1 GiB device copy (the counter scale reference), then "
                          "--steps OSK calls; for rocprofv3 --pmc passes.  skip-sweep: in-kernel skip "
@@ -231,12 +237,25 @@ def main():
                           "osk_calls": args.steps, "kernel_source_hash": kernel_source_hash()}))
         return
     if args.mode == "skip-sweep":
-        skip_sweep(args, wl, db, om, ml)
+        if args.mask == "kap":
+            om, ml = runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1)
+        skip_sweep(args, wl, db, om, ml, args.mask)
         return
     width = om.shape[2]
     ws_b = torch.empty(binding.cosa_build_order_mask_workspace_bytes(db.dims(width)), dtype=torch.uint8,
                        device="cuda")
     builder_ms, _ = time_calls(lambda: runner.build_mask(db, wl.budget1, workspace=ws_b), 5, 2)
+    kap_ms = None
+    if db.num_q_heads // db.num_kv_heads * (64 // KAP_STRIDE) <= 32:
+        # the KAP builder (CoSA section 4.2): stride 16, fixed fraction = the workload's budget, and Top-p 0.95
+        kw = binding.cosa_kap_mask_width(db.page_table.shape[1], binding.COSA_KAP_TOP_P, 0.95)
+        ws_k = torch.empty(binding.cosa_build_kap_mask_workspace_bytes(db.dims(kw)), dtype=torch.uint8, device="cuda")
+        kf, _ = time_calls(lambda: runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1,
+                                                         workspace=ws_k), 5, 2)
+        kp, _ = time_calls(lambda: runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_TOP_P, 0.95,
+                                                         workspace=ws_k), 5, 2)
+        kap_ms = {"stride": KAP_STRIDE, "fraction_ms": statistics.median(kf), "top_p_0.95_ms": statistics.median(kp)}
+        del ws_k
 
     # ---- one logged (untimed) call: visited / computed counts for the flop count
     logged = runner.prefill(db, om, ml, delta, log=True)
@@ -320,7 +339,7 @@ def main():
         "visited_q_head_pages": n_q_visits, "computed_q_head_pages": computed,
         "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
         "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
-        "dense": dense, "mask_builder_ms": statistics.median(builder_ms),
+        "dense": dense, "mask_builder_ms": statistics.median(builder_ms), "kap_builder": kap_ms,
         "osk_plus_builder_ms": med + statistics.median(builder_ms),
         "roofline": roofline, "attainable": attain, "cpu_baseline": cpu, "aborted_workgroups": aborts,
     }
