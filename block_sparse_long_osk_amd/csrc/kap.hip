@@ -18,7 +18,8 @@
 //              the 32 columns of S^T = K~ Q~^T tiles (v_mfma_f32_32x32x16_bf16,
 //              32 sampled keys per tile, read through the page table).  Pass 1:
 //              row maxima; pass 2: the same logits again (bitwise the same), block
-//              maxima, Pbar, the block sums over rows and heads, the HRM flags.
+//              maxima, Pbar, the block sums over rows and heads (DPP row sums),
+//              the HRM flags.
 //   kap_select one workgroup per (query block, KV head): the causal candidates'
 //              keys (HRM flag, score descending, id ascending) sorted bitonically
 //              in LDS; a fixed fraction or Top-p count; the mask row.
@@ -36,17 +37,54 @@ typedef __attribute__((ext_vector_type(16))) float kf32x16_t;
 typedef __attribute__((ext_vector_type(4))) int ki32x4_t;
 
 constexpr float kKapLog2e = 1.442695040888963407f;
+#ifndef KAP_COLUMN_TILES
+#define KAP_COLUMN_TILES 2
+#endif
+constexpr int kKapColumnTiles = KAP_COLUMN_TILES;  // column tiles of 32 query rows per wave
 
 __device__ __forceinline__ float kap_partner_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// One wave: query blocks i0 .. i0+BPW-1 of sequence `seq` (fewer at its end) and KV
-// head g.  Lane l holds query column n = l % 32 of the S^T tiles: block i0 + n / RB,
-// head n % RB / PER of the group, sampled row n % PER of the block; its 16
-// accumulator entries are the keys m = 8 (e / 4) + 4 (l / 32) + e % 4 of the tile.
-template <int PER>
+// Windowed sums over lane groups of rb = 2^k consecutive lanes with DPP row shifts
+// (bound_ctrl: lanes shifted in from outside the row read 0): the last lane of each
+// group ends with the group's total.  For rb = 32 a group is one half of the wave (two
+// 16-lane rows): the last lanes of its two rows are added, per half.
+__device__ __forceinline__ float group_sum(float v, int rb, int hi) {
+  if (rb > 1) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+  if (rb > 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
+  if (rb > 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));
+  if (rb > 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));
+  if (rb > 16) {
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float up = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    v = hi ? up : lo;
+  }
+  return v;
+}
+__device__ __forceinline__ int group_or(int v, int rb, int hi) {
+  if (rb > 1) v |= __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  if (rb > 2) v |= __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  if (rb > 4) v |= __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  if (rb > 8) v |= __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  if (rb > 16) {
+    const int lo = __builtin_amdgcn_readlane(v, 15) | __builtin_amdgcn_readlane(v, 31);
+    const int up = __builtin_amdgcn_readlane(v, 47) | __builtin_amdgcn_readlane(v, 63);
+    v = hi ? up : lo;
+  }
+  return v;
+}
+
+// One wave: query blocks i0 .. i0 + CT*BPW - 1 of sequence `seq` (fewer at its end)
+// and KV head g, as CT column tiles of 32.  In tile ct, lane l holds query column
+// n = l % 32: block i0 + ct*BPW + n / RB, head n % RB / PER of the group, sampled row
+// n % PER of the block; its 16 accumulator entries are the keys
+// m = 8 (e / 4) + 4 (l / 32) + e % 4 of the key tile.  Each key tile's operands are
+// read once and feed the CT column tiles.
+template <int PER, int CT>
 __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int G) {
   const int RB = G * PER;  // sampled rows per query block (all heads of the group)
   const int BPW = 32 / RB;
@@ -54,43 +92,46 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int G) {
   int seq = 0, base = 0;
   for (; seq < a.num_seqs; ++seq) {
     const int nb = a.cu_qblocks[seq + 1] - a.cu_qblocks[seq];
-    const int ng = (nb + BPW - 1) / BPW;
+    const int ng = (nb + CT * BPW - 1) / (CT * BPW);
     if (gi < base + ng) break;
     base += ng;
   }
   if (seq >= a.num_seqs) return;  // the grid is an upper bound on the group count
   const int qb_seq = a.cu_qblocks[seq];
   const int nqb = a.cu_qblocks[seq + 1] - qb_seq;
-  const int i0 = (gi - base) * BPW;
+  const int i0 = (gi - base) * CT * BPW;
   const int tok0 = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - tok0;
   const int R = (L + a.stride - 1) / a.stride;  // sampled positions of the sequence
   const int32_t* pt = a.page_table + (int64_t)seq * a.max_pages;
 
   const int n = lane & 31, hi = lane >> 5;
-  const int blk = n / RB, within = n % RB;
+  const int within = n % RB;
   const int hh = within / PER, sr = within % PER;
-  const int i = i0 + blk;
-  const int r = i * PER + sr;  // this column's sampled query position
-  const bool row_ok = blk < BPW && i < nqb && i < a.max_pages && r < R;
-
-  kbf16x8_t qf[8];
-  {
+  int i[CT], r[CT];
+  bool row_ok[CT], blk_ok[CT];
+  kbf16x8_t qf[CT][8];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    i[ct] = i0 + ct * BPW + n / RB;
+    r[ct] = i[ct] * PER + sr;  // this column's sampled query position
+    blk_ok[ct] = n / RB < BPW && i[ct] < nqb && i[ct] < a.max_pages;  // the column's query block exists
+    row_ok[ct] = blk_ok[ct] && r[ct] < R;                               // and so does its sampled row
     const uint16_t* qrow =
-        a.q + (int64_t)(tok0 + (int64_t)r * a.stride) * a.q_st + (int64_t)(g * G + hh) * a.q_sh + hi * 8;
+        a.q + (int64_t)(tok0 + (int64_t)r[ct] * a.stride) * a.q_st + (int64_t)(g * G + hh) * a.q_sh + hi * 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       ki32x4_t x = {0, 0, 0, 0};
-      if (row_ok) x = *(const ki32x4_t*)(qrow + c * 16);
-      qf[c] = __builtin_bit_cast(kbf16x8_t, x);
+      if (row_ok[ct]) x = *(const ki32x4_t*)(qrow + c * 16);
+      qf[ct][c] = __builtin_bit_cast(kbf16x8_t, x);
     }
   }
-  const int i_last = min(min(i0 + BPW, nqb), a.max_pages) - 1;
+  const int i_last = min(min(i0 + CT * BPW, nqb), a.max_pages) - 1;
   const int c_end = min(R, (i_last + 1) * PER);  // sampled keys any column may see
   const int n_tiles = (c_end + 31) / 32;
 
-  // S^T tile kt: keys 32 kt + m for the lane's 16 entries, in scaled-logit units
-  auto tile = [&](int kt, kf32x16_t& acc) {
+  // S^T tiles kt (keys 32 kt + m of the lane's 16 entries) for the CT column tiles
+  auto tile = [&](int kt, kf32x16_t (&acc)[CT]) {
     const int c = 32 * kt + n;  // the key this lane loads (A operand row)
     bool k_ok = c < R;
     int64_t off = 0;
@@ -101,64 +142,75 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int G) {
       k_ok = ph >= 0 && ph < a.num_phys;
       off = (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + (int64_t)(t % kPage) * a.kv_st + hi * 8;
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    kbf16x8_t ka[8];
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
       ki32x4_t x = {0, 0, 0, 0};
       if (k_ok) x = *(const ki32x4_t*)(a.k + off + cc * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(kbf16x8_t, x), qf[cc], acc, 0, 0, 0);
+      ka[cc] = __builtin_bit_cast(kbf16x8_t, x);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[cc], qf[ct][cc], acc[ct], 0, 0, 0);
     }
   };
-  // visibility of entry e of tile kt for this lane's column: sample c <= r (for a valid
+  // entry e of tile kt is visible to column r iff its key sample c <= r (for a valid
   // column r < R, so the key is a sample of the sequence)
-  auto visible = [&](int kt, int e) { return 32 * kt + 8 * (e >> 2) + 4 * hi + (e & 3) <= r; };
+  auto key_of = [&](int kt, int e) { return 32 * kt + 8 * (e >> 2) + 4 * hi + (e & 3); };
 
   // ---- pass 1: row maxima over the causal sampled keys
-  float M = -INFINITY;
+  float M[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) M[ct] = -INFINITY;
   for (int kt = 0; kt < n_tiles; ++kt) {
-    kf32x16_t acc;
+    kf32x16_t acc[CT];
     tile(kt, acc);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (visible(kt, e)) M = fmaxf(M, acc[e] * a.sm_scale);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (key_of(kt, e) <= r[ct]) M[ct] = fmaxf(M[ct], acc[ct][e] * a.sm_scale);
   }
-  M = kap_partner_max(M);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) M[ct] = kap_partner_max(M[ct]);
 
   // ---- pass 2: block maxima, Pbar = exp(m_rj - M_r), sums over the block's rows, flags
-  float* srow = a.score_rows + ((int64_t)(qb_seq + i) * a.hkv + g) * a.max_pages;
-  uint8_t* frow = a.flag_rows + ((int64_t)(qb_seq + i) * a.hkv + g) * a.max_pages;
   for (int kt = 0; kt < n_tiles; ++kt) {
-    kf32x16_t acc;
+    kf32x16_t acc[CT];
     tile(kt, acc);
-    // the lane's key blocks in this tile: PER = 4: block 8 kt + 2 q + hi from entries
-    // 4q .. 4q+3; PER = 8: block 4 kt + q from entries 4q .. 4q+3 of both lanes l, l^32
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      float mb = -INFINITY;
+    for (int ct = 0; ct < CT; ++ct) {
+      float* srow = a.score_rows + ((int64_t)(qb_seq + i[ct]) * a.hkv + g) * a.max_pages;
+      uint8_t* frow = a.flag_rows + ((int64_t)(qb_seq + i[ct]) * a.hkv + g) * a.max_pages;
+      // the lane's key blocks in this tile: PER = 4: block 8 kt + 2 q + hi from entries
+      // 4q .. 4q+3; PER = 8: block 4 kt + q from entries 4q .. 4q+3 of both lanes l, l^32
 #pragma unroll
-      for (int e = 4 * qq; e < 4 * qq + 4; ++e)
-        if (visible(kt, e)) mb = fmaxf(mb, acc[e] * a.sm_scale);
-      if (PER == 8) mb = kap_partner_max(mb);
-      const int j = PER == 4 ? 8 * kt + 2 * qq + hi : 4 * kt + qq;
-      const bool owner = row_ok && (PER == 4 || hi == 0);
-      float pbar = 0.f;
-      int hrm = 0;
-      if (owner && mb != -INFINITY) {
-        pbar = exp2f((mb - M) * kKapLog2e);
-        hrm = (mb == M) ? 1 : 0;
-      }
-      // sum and OR over the RB columns of the query block (consecutive lanes)
+      for (int qq = 0; qq < 4; ++qq) {
+        float mb = -INFINITY;
 #pragma unroll
-      for (int w = 1; w < 32; w <<= 1) {
-        if (w < RB) {
-          pbar += __shfl_xor(pbar, w, 64);
-          hrm |= __shfl_xor(hrm, w, 64);
+        for (int e = 4 * qq; e < 4 * qq + 4; ++e)
+          if (key_of(kt, e) <= r[ct]) mb = fmaxf(mb, acc[ct][e] * a.sm_scale);
+        if (PER == 8) mb = kap_partner_max(mb);
+        const int j = PER == 4 ? 8 * kt + 2 * qq + hi : 4 * kt + qq;
+        const bool owner = row_ok[ct] && (PER == 4 || hi == 0);
+        float pbar = 0.f;
+        int hrm = 0;
+        if (owner && mb != -INFINITY) {
+          pbar = exp2f((mb - M[ct]) * kKapLog2e);
+          hrm = (mb == M[ct]) ? 1 : 0;
         }
-      }
-      if (row_ok && within == 0 && (PER == 4 || hi == 0) && j <= i) {
-        srow[j] = pbar;
-        frow[j] = (uint8_t)hrm;
+        // sum and OR over the RB columns of the query block: consecutive lanes, an
+        // aligned group inside a 16-lane DPP row (RB <= 16) or two such rows (RB = 32)
+        pbar = group_sum(pbar, RB, hi);
+        hrm = group_or(hrm, RB, hi);
+        // the group's last lane writes (its own sampled row may lie past the sequence end)
+        if (blk_ok[ct] && within == RB - 1 && (PER == 4 || hi == 0) && j <= i[ct]) {
+          srow[j] = pbar;
+          frow[j] = (uint8_t)hrm;
+        }
       }
     }
   }
@@ -253,12 +305,12 @@ hipError_t launch_build_kap_mask(const KapArgs& a, hipStream_t stream) {
   if (a.total_qblocks == 0) return hipSuccess;
   const int G = a.hq / a.hkv;
   const int per = kPage / a.stride;
-  const int bpw = 32 / (G * per);
+  const int bpw = 32 / (G * per) * kKapColumnTiles;  // query blocks per wave
   const dim3 sgrid((unsigned)(a.total_qblocks / bpw + a.num_seqs), (unsigned)a.hkv);
   if (per == 4)
-    hipLaunchKernelGGL(kap_score_kernel<4>, sgrid, dim3(64), 0, stream, a, G);
+    hipLaunchKernelGGL((kap_score_kernel<4, kKapColumnTiles>), sgrid, dim3(64), 0, stream, a, G);
   else
-    hipLaunchKernelGGL(kap_score_kernel<8>, sgrid, dim3(64), 0, stream, a, G);
+    hipLaunchKernelGGL((kap_score_kernel<8, kKapColumnTiles>), sgrid, dim3(64), 0, stream, a, G);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int cap = 1;
