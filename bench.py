@@ -248,7 +248,7 @@ def main():
     kap_ms = None
     if db.num_q_heads // db.num_kv_heads * (64 // KAP_STRIDE) <= 32:
         # the KAP builder (CoSA section 4.2): stride 16, fixed fraction = the workload's budget, and Top-p 0.95
-        kw = binding.cosa_kap_mask_width(db.page_table.shape[1], binding.COSA_KAP_TOP_P, 0.95)
+        kw = binding.cosa_kap_mask_width(db.max_blocks, binding.COSA_KAP_TOP_P, 0.95)
         ws_k = torch.empty(binding.cosa_build_kap_mask_workspace_bytes(db.dims(kw)), dtype=torch.uint8, device="cuda")
         kf, _ = time_calls(lambda: runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1,
                                                          workspace=ws_k), 5, 2)

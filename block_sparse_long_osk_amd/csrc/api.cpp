@@ -20,16 +20,23 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool stride_ok(int64_t s) { return s > 0 && (s % 8) == 0; }
 
+// logical 64-token blocks a page-table row can address
+int32_t max_blocks(const cosa_osk_dims_t* d) {
+  return (int32_t)(((int64_t)d->max_pages_per_seq * d->page_size + kPage - 1) / kPage);
+}
+
 cosa_status_t check_dims(const cosa_osk_dims_t* d) {
   if (d == nullptr) return COSA_ERR_INVALID_ARG;
   if (d->reserved != 0) return COSA_ERR_INVALID_ARG;
   if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->total_q_tokens < 0 ||
       d->total_qblocks < 0 || d->max_pages_per_seq < 1 || d->num_phys_pages < 0 || d->max_mask_len < 0)
     return COSA_ERR_INVALID_ARG;
-  if (d->head_dim != kHeadDim || d->page_size != kPage) return COSA_ERR_UNSUPPORTED;
+  if (d->head_dim != kHeadDim) return COSA_ERR_UNSUPPORTED;
+  // physical pages of 16, 32 or 64 tokens; the logical block is always 64 tokens
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return COSA_ERR_UNSUPPORTED;
   if (d->num_q_heads % d->num_kv_heads != 0) return COSA_ERR_UNSUPPORTED;
   if (d->total_qblocks > cosa_osk::kMaxQBlocks || d->max_mask_len > cosa_osk::kMaxMaskLen ||
-      d->max_pages_per_seq > cosa_osk::kMaxPagesPerSeq)
+      max_blocks(d) > cosa_osk::kMaxPagesPerSeq)
     return COSA_ERR_UNSUPPORTED;
   // every query block holds 1..64 tokens
   if ((int64_t)d->total_q_tokens > (int64_t)kPage * d->total_qblocks || d->total_qblocks > d->total_q_tokens)
@@ -129,7 +136,9 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   a.hq = dims->num_q_heads;
   a.hkv = dims->num_kv_heads;
   a.total_qblocks = dims->total_qblocks;
-  a.max_pages = dims->max_pages_per_seq;
+  a.max_pages = max_blocks(dims);
+  a.pt_stride = dims->max_pages_per_seq;
+  a.page_len = dims->page_size;
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   a.sm_scale = resolved_scale(dims);
@@ -137,10 +146,10 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   return cosa_osk::launch_prefill(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
 }
 
-int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t flags) {
-  if (max_pages_per_seq < 1) return -1;
+int32_t cosa_order_mask_width(int32_t max_blocks_per_seq, float budget1, uint32_t flags) {
+  if (max_blocks_per_seq < 1) return -1;
   int32_t width = 0;
-  for (int32_t i = 0; i < max_pages_per_seq; ++i) {
+  for (int32_t i = 0; i < max_blocks_per_seq; ++i) {
     int nf = 0;
     if (flags & COSA_FORCE_FIRST) ++nf;
     if ((flags & COSA_FORCE_DIAG) && !((flags & COSA_FORCE_FIRST) && i == 0)) ++nf;
@@ -151,12 +160,12 @@ int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t
 }
 
 // builder workspace: pooled query and key proxies [total_qblocks, Hkv, 128] fp32 each,
-// then the score rows [total_qblocks, Hkv, max_pages_per_seq] fp32
+// then the score rows [total_qblocks, Hkv, max_blocks] fp32 (max_blocks: logical blocks per sequence)
 static size_t builder_pool_bytes(const cosa_osk_dims_t* d) {
   return round_up((size_t)d->total_qblocks * d->num_kv_heads * kHeadDim * sizeof(float) + 1);
 }
 static size_t builder_score_bytes(const cosa_osk_dims_t* d) {
-  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)(d->max_pages_per_seq > 0 ? d->max_pages_per_seq : 0) *
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)(d->max_pages_per_seq > 0 ? max_blocks(d) : 0) *
                       sizeof(float) + 1);
 }
 
@@ -172,13 +181,13 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
                                     hipStream_t stream) {
   cosa_status_t st = check_dims(dims);
   if (st != COSA_OK) return st;
-  if (dims->max_pages_per_seq > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
+  if (max_blocks(dims) > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
   if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
       order_mask == nullptr || mask_len == nullptr)
     return COSA_ERR_INVALID_ARG;
   if (!(budget1 >= 0.f && budget1 <= 1.f)) return COSA_ERR_INVALID_ARG;
   if ((flags & ~(uint32_t)(COSA_FORCE_FIRST | COSA_FORCE_DIAG)) != 0u) return COSA_ERR_INVALID_ARG;
-  if (dims->max_mask_len < cosa_order_mask_width(dims->max_pages_per_seq, budget1, flags)) return COSA_ERR_INVALID_ARG;
+  if (dims->max_mask_len < cosa_order_mask_width(max_blocks(dims), budget1, flags)) return COSA_ERR_INVALID_ARG;
   const size_t need = cosa_build_order_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
   cosa_osk::BuilderArgs a;
@@ -204,7 +213,9 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   a.hq = dims->num_q_heads;
   a.hkv = dims->num_kv_heads;
   a.total_qblocks = dims->total_qblocks;
-  a.max_pages = dims->max_pages_per_seq;
+  a.max_pages = max_blocks(dims);
+  a.pt_stride = dims->max_pages_per_seq;
+  a.page_len = dims->page_size;
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   a.budget1 = budget1;
@@ -212,21 +223,21 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   return cosa_osk::launch_build_order_mask(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
 }
 
-int32_t cosa_kap_mask_width(int32_t max_pages_per_seq, int32_t mode, float budget) {
-  if (max_pages_per_seq < 1) return -1;
-  if (mode == COSA_KAP_TOP_P) return max_pages_per_seq;
+int32_t cosa_kap_mask_width(int32_t max_blocks_per_seq, int32_t mode, float budget) {
+  if (max_blocks_per_seq < 1) return -1;
+  if (mode == COSA_KAP_TOP_P) return max_blocks_per_seq;
   if (mode != COSA_KAP_FRACTION) return -1;
-  const int w = (int)ceil((double)budget * (double)max_pages_per_seq - 1e-3);
-  return std::max(1, std::min(max_pages_per_seq, w));
+  const int w = (int)ceil((double)budget * (double)max_blocks_per_seq - 1e-3);
+  return std::max(1, std::min(max_blocks_per_seq, w));
 }
 
 // KAP workspace: fp32 score rows then uint8 flag rows, [total_qblocks, Hkv, max_pages] each
 static size_t kap_score_bytes(const cosa_osk_dims_t* d) {
-  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(d->max_pages_per_seq, 0) *
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(max_blocks(d), 0) *
                       sizeof(float) + 1);
 }
 static size_t kap_flag_bytes(const cosa_osk_dims_t* d) {
-  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(d->max_pages_per_seq, 0) + 1);
+  return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(max_blocks(d), 0) + 1);
 }
 
 size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims) {
@@ -241,7 +252,7 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
                                   size_t workspace_bytes, hipStream_t stream) {
   cosa_status_t st = check_dims(dims);
   if (st != COSA_OK) return st;
-  if (dims->max_pages_per_seq > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
+  if (max_blocks(dims) > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
   if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
       order_mask == nullptr || mask_len == nullptr)
     return COSA_ERR_INVALID_ARG;
@@ -254,7 +265,7 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   // of at most 32 MFMA columns
   const int rb = G * (cosa_osk::kPage / stride);
   if (rb > 32 || (rb & (rb - 1)) != 0) return COSA_ERR_UNSUPPORTED;
-  if (dims->max_mask_len < cosa_kap_mask_width(dims->max_pages_per_seq, mode, budget)) return COSA_ERR_INVALID_ARG;
+  if (dims->max_mask_len < cosa_kap_mask_width(max_blocks(dims), mode, budget)) return COSA_ERR_INVALID_ARG;
   const size_t need = cosa_build_kap_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
   cosa_osk::KapArgs a;
@@ -279,7 +290,9 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   a.hq = dims->num_q_heads;
   a.hkv = dims->num_kv_heads;
   a.total_qblocks = dims->total_qblocks;
-  a.max_pages = dims->max_pages_per_seq;
+  a.max_pages = max_blocks(dims);
+  a.pt_stride = dims->max_pages_per_seq;
+  a.page_len = dims->page_size;
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   a.stride = stride;
@@ -308,7 +321,9 @@ cosa_status_t cosa_validate_order_mask(const cosa_osk_dims_t* dims, const int32_
   a.num_seqs = dims->num_seqs;
   a.hkv = dims->num_kv_heads;
   a.total_qblocks = dims->total_qblocks;
-  a.max_pages = dims->max_pages_per_seq;
+  a.max_pages = max_blocks(dims);
+  a.pt_stride = dims->max_pages_per_seq;
+  a.page_len = dims->page_size;
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   return cosa_osk::launch_validate(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int G) {
   const int tok0 = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - tok0;
   const int R = (L + a.stride - 1) / a.stride;  // sampled positions of the sequence
-  const int32_t* pt = a.page_table + (int64_t)seq * a.max_pages;
+  const int32_t* pt = a.page_table + (int64_t)seq * a.pt_stride;
 
   const int n = lane & 31, hi = lane >> 5;
   const int within = n % RB;
@@ -137,10 +137,10 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int G) {
     int64_t off = 0;
     if (k_ok) {
       const int t = c * a.stride;
-      const int page = t / kPage;
-      const int ph = page < a.max_pages ? pt[page] : -1;
+      const int page = t / a.page_len;  // physical page of token t
+      const int ph = page < a.pt_stride ? pt[page] : -1;
       k_ok = ph >= 0 && ph < a.num_phys;
-      off = (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + (int64_t)(t % kPage) * a.kv_st + hi * 8;
+      off = (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + (int64_t)(t % a.page_len) * a.kv_st + hi * 8;
     }
     kbf16x8_t ka[8];
 #pragma unroll

@@ -72,14 +72,17 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
     a.qbar[((int64_t)qb * a.hkv + g) * kHeadDim + tid] = t / (float)rows;
   }
   __syncthreads();
-  // ---- kbar: mean of the same-index logical page's keys
-  const int ph = i < a.max_pages ? a.page_table[(int64_t)s * a.max_pages + i] : -1;
-  const bool has_page = ph >= 0 && ph < a.num_phys;
+  // ---- kbar: mean of the same-index logical block's keys (through its physical pages)
+  const int32_t* pt_row = a.page_table + (int64_t)s * a.pt_stride;
+  int ph[4] = {-1, -1, -1, -1};
+  const bool has_page = i < a.max_pages && block_phys(pt_row, a.pt_stride, i, L, a.page_len, a.num_phys, ph);
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   if (has_page) {
-    const uint16_t* kp = a.k + (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh + chunk * 8;
-    for (int t = rg; t < rows; t += 16) add8(acc, kp + (int64_t)t * a.kv_st);
+    for (int t = rg; t < rows; t += 16) {
+      const uint16_t* kp = a.k + (int64_t)ph[t / a.page_len] * a.kv_sp + (int64_t)g * a.kv_sh + chunk * 8;
+      add8(acc, kp + (int64_t)(t % a.page_len) * a.kv_st);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg][chunk * 8 + e] = acc[e];
@@ -266,8 +269,9 @@ __global__ __launch_bounds__(64) void validate_kernel(const ValidateArgs a) {
     if (id > i) ++c_causal;
     const uint32_t bit = 1u << (id & 31);
     if (atomicOr(&seen[id >> 5], bit) & bit) ++c_dup;
-    const int ph = a.page_table[(int64_t)s * a.max_pages + id];
-    if (ph < 0 || ph >= a.num_phys) ++c_phys;
+    int ph[4];
+    if (!block_phys(a.page_table + (int64_t)s * a.pt_stride, a.pt_stride, id, L, a.page_len, a.num_phys, ph))
+      ++c_phys;
   }
   // reduce over the wave, one atomic per counter
   const int vals[5] = {c_range, c_causal, c_dup, c_len, c_phys};

@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "osk_internal.h"
 
 namespace cosa_osk {
@@ -53,7 +55,10 @@ typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
 constexpr int kTileBytes = kPage * kHeadDim * 2;  // one K or V page of one KV head: 16 KiB
 constexpr int kPageBytes = 2 * kTileBytes;        // K then V
-constexpr int kWindow = 512;                      // mask entries resolved per window
+// mask entries resolved per window: 512, or 256 when a logical block spans several
+// physical pages (their ids take LDS)
+template <int SUB>
+constexpr int window_len() { return SUB == 1 ? 512 : 256; }
 constexpr int kRing = 4;                          // page slots in flight per workgroup
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -163,25 +168,40 @@ struct TileGather {
       lane_k[x] = (uint32_t)(trow * kv_st + swz_k(4 * (x * NW + wave) + trow, lane & 15) * 8) * 2u;
     lane_v = (uint32_t)(trow * kv_st + swz_v(trow, lane & 15) * 8) * 2u;
   }
-  // this wave's share of one tile (valid_rows rows hold data) into the slot at LDS byte address slot
-  __device__ __forceinline__ void issue(const uint16_t* tile, uint32_t slot, int valid_rows, bool is_v, int wave,
-                                        int lane) const {
+  // This wave's share of one tile (valid_rows rows hold data) into the slot at LDS byte
+  // address slot.  sub_base[s] is the tile's base in physical page s of the logical
+  // block (page_len tokens each, SUB = 64 / page_len pages); the 4 rows of a 1-KiB
+  // block always lie in one physical page.
+  template <int SUB>
+  __device__ __forceinline__ void issue(const uint16_t* const (&sub_base)[SUB], int page_len, uint32_t slot,
+                                        int valid_rows, bool is_v, int wave, int lane) const {
     if (valid_rows >= kPage) {
 #pragma unroll
       for (int x = 0; x < kBlocks; ++x) {
         const int b = x * NW + wave;
-        dma_16B_saddr(tile + 4 * b * kv_st, is_v ? lane_v : lane_k[x & 1], slot + (uint32_t)b * 1024u);
+        const int row = 4 * b;
+        const uint16_t* base = SUB == 1 ? sub_base[0] + row * kv_st
+                                        : sub_base[row / page_len] + (row % page_len) * kv_st;
+        dma_16B_saddr(base, is_v ? lane_v : lane_k[x & 1], slot + (uint32_t)b * 1024u);
       }
     } else {
-      // rare: the lane terms are recomputed here rather than kept in registers
+      // Tail block: rows at or past the valid count read a valid row instead -- the
+      // block's own first row when the block straddles the end, row 0 of the logical
+      // block when it lies wholly past it -- so their (masked) values stay finite.  Rare:
+      // the lane terms are recomputed here rather than kept in registers.
       const int ln = (int)opaque((uint32_t)lane);
 #pragma unroll
       for (int x = 0; x < kBlocks; ++x) {
         const int b = x * NW + wave;
-        const int t = 4 * b + (ln >> 4);
-        const int ts = t < valid_rows ? t : 0;
+        const int row = 4 * b;
+        const bool past = row >= valid_rows;
+        const uint16_t* base = past ? sub_base[0]
+                                    : (SUB == 1 ? sub_base[0] + row * kv_st
+                                                : sub_base[row / page_len] + (row % page_len) * kv_st);
+        const int t = row + (ln >> 4);
+        const int ts = (past || t >= valid_rows) ? 0 : t - row;  // row within the addressed group
         const uint32_t voff = (uint32_t)(ts * kv_st + (is_v ? swz_v(t, ln & 15) : swz_k(t, ln & 15)) * 8) * 2u;
-        dma_16B_saddr(tile, voff, slot + (uint32_t)b * 1024u);
+        dma_16B_saddr(base, voff, slot + (uint32_t)b * 1024u);
       }
     }
   }
@@ -326,7 +346,7 @@ __device__ __forceinline__ Unit decode_unit(const PrefillArgs& a, int heads_per_
   // for well-formed inputs; the clamp keeps every table and bitmap access in bounds)
   u.n_pages = min((u.L + kPage - 1) / kPage, a.max_pages);
   u.len = min(max(a.mask_len[(int64_t)u.qb * a.hkv + u.g], 0), a.max_mask_len);
-  u.pt_row = a.page_table + (int64_t)lo * a.max_pages;
+  u.pt_row = a.page_table + (int64_t)lo * a.pt_stride;
   return u;
 }
 
@@ -347,33 +367,42 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Unit& u, int 
 }
 
 // Visit list of one window of the mask row, in LDS.
+template <int SUB>
 struct WindowLds {
-  int raw_id[kWindow];
-  int raw_phys[kWindow];
-  int vis_phys[kWindow];
-  int vis_j[kWindow];
-  int vis_k[kWindow];
+  static constexpr int kWin = window_len<SUB>();
+  int raw_id[kWin];
+  int raw_phys[kWin * SUB];  // physical pages of each entry's logical block
+  int vis_phys[kWin * SUB];
+  int vis_j[kWin];
+  int vis_k[kWin];
   uint32_t seen_bits[kMaxPagesPerSeq / 32];
   int count;
 };
 
 // Resolve mask entries k0 .. k0+wl-1 into the window's visit list: an entry is
-// visited when its id is a causal page of the sequence (0 <= id <= i, id below the
-// page count) with a valid physical page, and only at its first occurrence in the
-// row (bitmap over the sequence's pages, kept across windows).  Returns the number
-// of visits.  Called by every thread of the workgroup; ends with a barrier.
-template <int NT>
+// visited when its id is a causal logical block of the sequence (0 <= id <= i, id
+// below the block count) whose physical pages are valid, and only at its first
+// occurrence in the row (bitmap over the sequence's blocks, kept across windows).
+// Returns the number of visits.  Called by every thread of the workgroup; ends with
+// a barrier.
+template <int NT, int SUB>
 __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& u, const int32_t* mrow, int k0,
-                                              int wl, WindowLds& w, int wave, int lane) {
+                                              int wl, WindowLds<SUB>& w, int wave, int lane) {
   for (int e = threadIdx.x; e < wl; e += NT) {
     const int id = mrow[k0 + e];
-    int ph = -1;
+    int ph[SUB];
+    bool ok = false;
     if (id >= 0 && id < u.n_pages && id <= u.i) {
-      ph = u.pt_row[id];
-      if (ph < 0 || ph >= a.num_phys) ph = -1;
+      if (SUB == 1) {
+        ph[0] = u.pt_row[id];
+        ok = ph[0] >= 0 && ph[0] < a.num_phys;
+      } else {
+        ok = block_phys(u.pt_row, a.pt_stride, id, u.L, a.page_len, a.num_phys, ph);
+      }
     }
-    w.raw_id[e] = ph >= 0 ? id : -1;
-    w.raw_phys[e] = ph;
+    w.raw_id[e] = ok ? id : -1;
+#pragma unroll
+    for (int x = 0; x < SUB; ++x) w.raw_phys[e * SUB + x] = ok ? ph[x] : -1;
   }
   __syncthreads();
   // wave 0 compacts the visited entries in mask order
@@ -400,7 +429,8 @@ __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& 
       const uint64_t km = __ballot(keep);
       if (keep) {
         const int p = count + __popcll(km & ((1ull << lane) - 1ull));
-        w.vis_phys[p] = w.raw_phys[e];
+#pragma unroll
+        for (int x = 0; x < SUB; ++x) w.vis_phys[p * SUB + x] = w.raw_phys[e * SUB + x];
         w.vis_j[p] = id;
         w.vis_k[p] = k0 + e;
       }
@@ -595,15 +625,16 @@ __device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
 // before the barrier), the block vote from both halves' margins, and the value
 // side of page v unless it is skipped.  Every wave runs the same number of
 // barriers (the visit count is workgroup-uniform), so no wait can hang.
-template <int HW>
+template <int HW, int SUB>
 __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const PrefillArgs a, int heads_per_group,
                                                                     int nsub) {
   constexpr int NW = 2 * HW;   // waves
   constexpr int NT = 64 * NW;  // threads
   constexpr int GW = NW >= 4 ? NW / 2 : NW;  // waves that gather pages (waves 0 .. GW-1)
   constexpr int PW = 32 / GW;                 // page-gather instructions per gathering wave per page
+  constexpr int kWindow = window_len<SUB>();  // SUB: physical pages per logical block
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
-  __shared__ WindowLds wlds;
+  __shared__ WindowLds<SUB> wlds;
   __shared__ uint8_t dec_lds[HW][kWindow];
   __shared__ float mar_lds[HW][kWindow];
   __shared__ float vote_val[HW][2][2];
@@ -649,16 +680,29 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     const int wl = min(kWindow, u.len - k0);
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
-    const int nv = resolve_window<NT>(a, u, mrow, k0, wl, wlds, wave, lane);
-    auto gather = [&](int p) {
-      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]);
-      const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(wlds.vis_phys[p]) * a.kv_sp;
+    const int nv = resolve_window<NT, SUB>(a, u, mrow, k0, wl, wlds, wave, lane);
+    // this wave's share of visit p's K and V tiles (phys: the block's physical pages)
+    auto gather_tiles = [&](int jp, const int (&phys)[SUB], int p) {
       const uint32_t slot = ring_addr + (uint32_t)(p % kRing) * kPageBytes;
       const int valid_rows = u.L - jp * kPage;
-      if (gatherer) {
-        tg.issue(kbase + off, slot, valid_rows, false, wave, lane);
-        tg.issue(vbase + off, slot + kTileBytes, valid_rows, true, wave, lane);
+      const uint16_t* kb_sub[SUB];
+      const uint16_t* vb_sub[SUB];
+#pragma unroll
+      for (int x = 0; x < SUB; ++x) {
+        const int64_t off = (int64_t)phys[x] * a.kv_sp;
+        kb_sub[x] = kbase + off;
+        vb_sub[x] = vbase + off;
       }
+      tg.template issue<SUB>(kb_sub, a.page_len, slot, valid_rows, false, wave, lane);
+      tg.template issue<SUB>(vb_sub, a.page_len, slot + kTileBytes, valid_rows, true, wave, lane);
+    };
+    auto gather = [&](int p) {
+      if (!gatherer) return;
+      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]);
+      int phys[SUB];
+#pragma unroll
+      for (int x = 0; x < SUB; ++x) phys[x] = __builtin_amdgcn_readfirstlane(wlds.vis_phys[p * SUB + x]);
+      gather_tiles(jp, phys, p);
     };
 
     // ---- prologue: gather pages 0 .. kRing-2; page 0 resident before the first QK
@@ -675,7 +719,9 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       // does not wait on LDS (index clamped inside the window when there is no such page)
       const int pg = min(v + kRing - 1, kWindow - 1);
       const int pg_j = wlds.vis_j[pg];
-      const int pg_phys = wlds.vis_phys[pg];
+      int pg_phys[SUB];
+#pragma unroll
+      for (int x = 0; x < SUB; ++x) pg_phys[x] = wlds.vis_phys[pg * SUB + x];
       const int j = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
       const uint32_t kb = ring_addr + (uint32_t)slot * kPageBytes;
       const uint32_t vb = kb + kTileBytes;
@@ -697,12 +743,10 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       lds_barrier();
       const float partner = vote ? vote_val[hl][half ^ 1][par] : -INFINITY;
       if (gatherer && v + kRing - 1 < nv) {
-        const int jp = __builtin_amdgcn_readfirstlane(pg_j);
-        const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(pg_phys) * a.kv_sp;
-        const uint32_t gslot = ring_addr + (uint32_t)((v + kRing - 1) % kRing) * kPageBytes;
-        const int valid_rows = u.L - jp * kPage;
-        tg.issue(kbase + off, gslot, valid_rows, false, wave, lane);
-        tg.issue(vbase + off, gslot + kTileBytes, valid_rows, true, wave, lane);
+        int phys[SUB];
+#pragma unroll
+        for (int x = 0; x < SUB; ++x) phys[x] = __builtin_amdgcn_readfirstlane(pg_phys[x]);
+        gather_tiles(__builtin_amdgcn_readfirstlane(pg_j), phys, v + kRing - 1);
       }
       const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(partner))));
       const bool skip = skip_on && (margin2 < tau2);
@@ -737,12 +781,19 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 grid((unsigned)a.total_qblocks * (unsigned)a.hkv * (unsigned)nsub);
-  if (HW == 4)
-    hipLaunchKernelGGL(osk_prefill_ring_kernel<4>, grid, dim3(512), 0, stream, a, G, nsub);
-  else if (HW == 2)
-    hipLaunchKernelGGL(osk_prefill_ring_kernel<2>, grid, dim3(256), 0, stream, a, G, nsub);
-  else
-    hipLaunchKernelGGL(osk_prefill_ring_kernel<1>, grid, dim3(128), 0, stream, a, G, nsub);
+  const int sub = kPage / a.page_len;
+  auto launch = [&](auto hw_c, auto sub_c) {
+    constexpr int H = decltype(hw_c)::value, S = decltype(sub_c)::value;
+    hipLaunchKernelGGL((osk_prefill_ring_kernel<H, S>), grid, dim3(128 * H), 0, stream, a, G, nsub);
+  };
+  auto by_sub = [&](auto hw_c) {
+    if (sub == 1) launch(hw_c, std::integral_constant<int, 1>{});
+    else if (sub == 2) launch(hw_c, std::integral_constant<int, 2>{});
+    else launch(hw_c, std::integral_constant<int, 4>{});
+  };
+  if (HW == 4) by_sub(std::integral_constant<int, 4>{});
+  else if (HW == 2) by_sub(std::integral_constant<int, 2>{});
+  else by_sub(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

@@ -78,6 +78,8 @@ class Workload:
     pool_seed: Optional[int] = None
     pool_pages: Optional[int] = None
     skipping: bool = True     # False: skip scale fixed at -1 (disabled)
+    page_size: int = 64       # tokens per physical KV page (16 or 32: the same tokens re-paged)
+    tokens_of: Optional[str] = None  # workload whose tokens these are (re-paged): its skip scale applies
 
     @property
     def total_tokens(self) -> int:
@@ -103,6 +105,12 @@ WORKLOADS: Dict[str, Workload] = {
         (131072, 65536), 32, 8, "structured", (1005, 1006), 0.10,
         pool="shuffled", pool_seed=1007, pool_pages=3072),
 }
+# The 128K workload with its KV cache in 16-token physical pages (four per logical block),
+# shuffled: the same tokens, a different storage layout.
+WORKLOADS["cfg4_128k_structured_p16"] = dataclasses.replace(
+    WORKLOADS["cfg4_128k_structured"], name="cfg4_128k_structured_p16",
+    description="cfg4_128k_structured with its KV cache in shuffled 16-token physical pages",
+    page_size=16, pool_seed=1008, tokens_of="cfg4_128k_structured")
 WORKLOAD_ORDER = ["cfg1_2k_mha", "cfg2_16k_gqa", "cfg3_32k_structured",
                   "cfg4_128k_structured", "cfg5_paged_2seq"]
 
@@ -143,7 +151,13 @@ class Batch:
 
     @property
     def max_pages(self) -> int:
+        """Page-table row length (physical pages per sequence)."""
         return int(self.page_table.shape[1])
+
+    @property
+    def max_blocks(self) -> int:
+        """Logical 64-token blocks a page-table row addresses."""
+        return -(-self.max_pages * int(self.k_pool.shape[2]) // PAGE)
 
 
 def _unit_rows(rng: np.random.Generator, n: int, d: int) -> np.ndarray:
@@ -251,7 +265,40 @@ def generate(wl: Workload) -> Batch:
         if rem:
             k_bits[ph[n_full], :, :rem, :] = kb[n_full * PAGE:].transpose(1, 0, 2)
             v_bits[ph[n_full], :, :rem, :] = vb[n_full * PAGE:].transpose(1, 0, 2)
-    return Batch(wl, q_bits, k_bits, v_bits, page_table, cu_seqlens, cu_qblocks, salient_all)
+    bt = Batch(wl, q_bits, k_bits, v_bits, page_table, cu_seqlens, cu_qblocks, salient_all)
+    if wl.page_size != PAGE:
+        bt = repage(bt, wl.page_size, wl.pool_seed if wl.pool_seed is not None else 0)
+    return bt
+
+
+def repage(batch: Batch, page_size: int, seed: int) -> Batch:
+    """The same token rows stored in a pool of page_size-token physical pages (16 or 32;
+    a storage layout change only): the page-sized token ranges of every sequence go to
+    physical pages in the order of a permutation drawn from (seed, stream 4), with 3
+    spare pages; page-table rows are -1 padded."""
+    if PAGE % page_size != 0 or page_size == PAGE:
+        raise ValueError("page_size must be 16 or 32")
+    sub = PAGE // page_size
+    S = batch.num_seqs
+    lens = np.diff(batch.cu_seqlens.astype(np.int64))
+    n_small = [int(-(-L // page_size)) for L in lens]
+    total = sum(n_small)
+    perm = np.random.default_rng([seed, STREAM_POOL]).permutation(total + 3)
+    hkv, d = batch.k_pool.shape[1], batch.k_pool.shape[3]
+    k_new = np.zeros((total + 3, hkv, page_size, d), dtype=batch.k_pool.dtype)
+    v_new = np.zeros_like(k_new)
+    pt = np.full((S, batch.page_table.shape[1] * sub), -1, dtype=np.int32)
+    pos = 0
+    for s in range(S):
+        for p in range(n_small[s]):
+            src = batch.page_table[s, p // sub]
+            r0 = (p % sub) * page_size
+            dst = perm[pos]
+            k_new[dst] = batch.k_pool[src, :, r0:r0 + page_size]
+            v_new[dst] = batch.v_pool[src, :, r0:r0 + page_size]
+            pt[s, p] = dst
+            pos += 1
+    return dataclasses.replace(batch, k_pool=k_new, v_pool=v_new, page_table=pt)
 
 
 # ----------------------------------------------------------------------------
@@ -268,4 +315,4 @@ def skip_scale(name: str) -> float:
         return -1.0
     with open(_DELTA_FILE) as f:
         table = json.load(f)
-    return float(table[name]["delta"])
+    return float(table[wl.tokens_of or name]["delta"])

@@ -15,9 +15,9 @@ from .binding import COSA_FORCE_DIAG, COSA_FORCE_FIRST
 @dataclasses.dataclass
 class DeviceBatch:
     q: "torch.Tensor"            # bf16 [T, Hq, 128]
-    k_pool: "torch.Tensor"       # bf16 [n_phys, Hkv, 64, 128]
+    k_pool: "torch.Tensor"       # bf16 [n_phys, Hkv, page_size, 128]
     v_pool: "torch.Tensor"
-    page_table: "torch.Tensor"   # int32 [S, max_pages]
+    page_table: "torch.Tensor"   # int32 [S, physical pages per sequence]
     cu_seqlens: "torch.Tensor"   # int32 [S+1]
     cu_qblocks: "torch.Tensor"   # int32 [S+1]
     total_qblocks: int
@@ -30,6 +30,11 @@ class DeviceBatch:
     @property
     def num_q_heads(self) -> int:
         return self.q.shape[1]
+
+    @property
+    def max_blocks(self) -> int:
+        """Logical 64-token blocks a page-table row addresses (mask ids, score rows)."""
+        return -(-self.page_table.shape[1] * self.k_pool.shape[2] // 64)
 
     def dims(self, max_mask_len: int, sm_scale: float = 0.0) -> binding.CosaOskDims:
         return binding.make_dims(self.q, self.k_pool, self.page_table, self.total_qblocks, max_mask_len,
@@ -111,7 +116,7 @@ def build_mask(db: DeviceBatch, budget1: float, flags: int = COSA_FORCE_FIRST | 
                width: Optional[int] = None, scores: bool = False, workspace=None, stream=None):
     """cosa_build_order_mask on the device batch; returns (order_mask, mask_len[, scores])."""
     import torch
-    max_pages = db.page_table.shape[1]
+    max_pages = db.max_blocks
     if width is None:
         width = binding.cosa_order_mask_width(max_pages, budget1, flags)
     dims = db.dims(width)
@@ -128,7 +133,7 @@ def build_kap_mask(db: DeviceBatch, stride: int, mode: int, budget: float, width
                    outputs: bool = False, workspace=None, stream=None):
     """cosa_build_kap_mask on the device batch; returns (order_mask, mask_len[, scores, flags])."""
     import torch
-    max_pages = db.page_table.shape[1]
+    max_pages = db.max_blocks
     if width is None:
         width = binding.cosa_kap_mask_width(max_pages, mode, budget)
     dims = db.dims(width)

@@ -29,17 +29,29 @@
  *   a launch failure is reported as COSA_ERR_HIP.
  * - The library keeps no state between calls; calls are thread-safe.  Calls
  *   that share a workspace must be ordered on one stream.
- * - Supported: head_dim = 128, page_size = 64 (the query block equals the KV
- *   page), bfloat16 Q/K/V/out, num_q_heads % num_kv_heads == 0.
+ * - Blocks and pages (CoSA Appendix D.1: the logical block size b and the
+ *   physical KV-cache page size b_p are set independently; a logical block is
+ *   resolved through one or more physical pages).  The logical block -- the query
+ *   block, the mask's key block, the unit of a skip vote -- is b = 64 tokens.  The
+ *   KV cache's physical pages hold b_p = page_size = 16, 32 or 64 tokens: logical
+ *   block j of a sequence is its tokens 64 j .. 64 j + 63, token t stored in
+ *   physical page page_table[s][t / b_p] at row t % b_p.  A logical block is used
+ *   only if every physical page holding one of its tokens t < L is a valid page id
+ *   (0 <= id < num_phys_pages); otherwise it is not visited, like an invalid id.
+ *   max_blocks = ceil(max_pages_per_seq * page_size / 64) logical blocks per
+ *   sequence are addressable; mask ids, the mask-width helpers and the builders'
+ *   score rows count logical blocks.
+ * - Supported: head_dim = 128, page_size 16, 32 or 64, bfloat16 Q/K/V/out,
+ *   num_q_heads % num_kv_heads == 0.
  *   Limits: total_qblocks <= 16384, max_mask_len <= 8191,
- *   max_pages_per_seq <= 16384 (<= 8192 for the mask builder),
+ *   max_blocks <= 16384 (<= 8192 for the mask builders),
  *   kv_stride_tok <= 2^24 elements (a page's byte offsets fit in 32 bits).
  *   Anything else returns COSA_ERR_UNSUPPORTED.
  * - Layouts (element strides; head_dim is contiguous; strides are multiples of
  *   8 elements and the base pointers are 16-byte aligned):
  *     q, out        [total_q_tokens, num_q_heads, 128]   (sequences packed on T)
- *     k_pool,v_pool [num_phys_pages, num_kv_heads, 64, 128] (same strides)
- *     page_table    int32 [num_seqs, max_pages_per_seq]   logical -> physical page
+ *     k_pool,v_pool [num_phys_pages, num_kv_heads, page_size, 128] (same strides)
+ *     page_table    int32 [num_seqs, max_pages_per_seq]   page-sized token range -> physical page
  *     cu_seqlens    int32 [num_seqs + 1]  token offsets; L_s = difference
  *     cu_qblocks    int32 [num_seqs + 1]  prefix sums of ceil(L_s / 64)
  *     order_mask    int32 [total_qblocks, num_kv_heads, max_mask_len]
@@ -84,10 +96,10 @@ typedef struct cosa_osk_dims {
   int32_t num_q_heads;        /* Hq */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;           /* must be 128 */
-  int32_t page_size;          /* must be 64 */
+  int32_t page_size;          /* tokens per physical KV page: 16, 32 or 64 */
   int32_t total_q_tokens;     /* T = cu_seqlens[num_seqs] */
   int32_t total_qblocks;      /* cu_qblocks[num_seqs] */
-  int32_t max_pages_per_seq;  /* row stride of page_table */
+  int32_t max_pages_per_seq;  /* row stride of page_table (physical pages per sequence) */
   int32_t num_phys_pages;     /* pool size; a physical id outside [0, n) is not visited */
   int32_t max_mask_len;       /* row stride of order_mask and of the decision log */
   float sm_scale;             /* logit scale; <= 0 selects 1/sqrt(head_dim) */
@@ -156,15 +168,16 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims,
 
 /*
  * Row width a computation-order mask built by cosa_build_order_mask needs:
- * the longest |F_i| + ceil(budget1 * |R_i| - 1e-3) over blocks i < max_pages_per_seq
+ * the longest |F_i| + ceil(budget1 * |R_i| - 1e-3) over blocks i < max_blocks_per_seq
  * (F_i: forced pages, R_i: the other causal pages).  Host-only.  Returns -1 for
- * max_pages_per_seq < 1.
+ * max_blocks_per_seq < 1.  (max_blocks_per_seq: logical blocks per sequence, the
+ * max_blocks of the dims.)
  */
-int32_t cosa_order_mask_width(int32_t max_pages_per_seq, float budget1, uint32_t flags);
+int32_t cosa_order_mask_width(int32_t max_blocks_per_seq, float budget1, uint32_t flags);
 
 /* Workspace bytes cosa_build_order_mask needs: the fp32 pooled query and key
  * proxies [total_qblocks, Hkv, 128] each and the fp32 score rows
- * [total_qblocks, Hkv, max_pages_per_seq] (used when proxy_scores is NULL),
+ * [total_qblocks, Hkv, max_blocks] (used when proxy_scores is NULL),
  * each region padded to 256 bytes.  Host-only. */
 size_t cosa_build_order_mask_workspace_bytes(const cosa_osk_dims_t* dims);
 
@@ -182,7 +195,7 @@ size_t cosa_build_order_mask_workspace_bytes(const cosa_osk_dims_t* dims);
  *   the row lists the kept ids in (score descending, id ascending) order, -1 after.
  * order_mask [total_qblocks, Hkv, max_mask_len] and mask_len [total_qblocks, Hkv]
  * are written; dims->max_mask_len must be >= cosa_order_mask_width(...).
- * proxy_scores (nullable) fp32 [total_qblocks, Hkv, max_pages_per_seq]: score_j for
+ * proxy_scores (nullable) fp32 [total_qblocks, Hkv, max_blocks]: score_j for
  * j <= i, NaN after.  budget1 in [0, 1].  k_pool uses the dims' KV strides.
  */
 cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
@@ -195,13 +208,14 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
 #define COSA_KAP_FRACTION 0 /* K_i = ceil(budget * (i + 1) - 1e-3), at least 1            */
 #define COSA_KAP_TOP_P 1    /* smallest K_i whose leading scores reach budget of the total */
 
-/* Row width a KAP mask needs: ceil(budget * max_pages - 1e-3) clamped to
- * [1, max_pages] for COSA_KAP_FRACTION, max_pages for COSA_KAP_TOP_P.  Host-only.
- * Returns -1 for max_pages_per_seq < 1 or an unknown mode. */
-int32_t cosa_kap_mask_width(int32_t max_pages_per_seq, int32_t mode, float budget);
+/* Row width a KAP mask needs: ceil(budget * max_blocks - 1e-3) clamped to
+ * [1, max_blocks] for COSA_KAP_FRACTION, max_blocks for COSA_KAP_TOP_P (max_blocks:
+ * logical blocks per sequence).  Host-only.  Returns -1 for max_blocks_per_seq < 1
+ * or an unknown mode. */
+int32_t cosa_kap_mask_width(int32_t max_blocks_per_seq, int32_t mode, float budget);
 
 /* Workspace bytes cosa_build_kap_mask needs: fp32 block scores and uint8 HRM flags
- * [total_qblocks, Hkv, max_pages_per_seq] each, each region padded to 256 bytes
+ * [total_qblocks, Hkv, max_blocks] each, each region padded to 256 bytes
  * (used where the caller passes no array of its own).  Host-only. */
 size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims);
 
@@ -223,9 +237,9 @@ size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims);
  * order_mask [total_qblocks, Hkv, max_mask_len] and mask_len [total_qblocks, Hkv]
  * are written; dims->max_mask_len must be >= cosa_kap_mask_width(...).
  * kap_scores (nullable) fp32 and hrm_flags (nullable) uint8, both
- * [total_qblocks, Hkv, max_pages_per_seq]: s_ij and h_ij for j <= i, NaN / 0 after.
+ * [total_qblocks, Hkv, max_blocks]: s_ij and h_ij for j <= i, NaN / 0 after.
  * Supported: stride 8 or 16, and G * 64 / stride a power of two <= 32 (G = Hq / Hkv);
- * max_pages_per_seq <= 8192; otherwise COSA_ERR_UNSUPPORTED.  The page-table entries
+ * max_blocks <= 8192; otherwise COSA_ERR_UNSUPPORTED.  The page-table entries
  * of a sequence's pages must be valid physical pages.  k_pool uses the dims' KV
  * strides.  Asynchronous on `stream`; the workspace is overwritten.
  */

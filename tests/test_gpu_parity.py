@@ -203,7 +203,7 @@ def _builder_parity(rt, name, bt, ref_om, ref_ml):
     om, ml = om.cpu().numpy(), ml.cpu().numpy()
     # fp64 reference scores of every causal (block, page) pair
     prox = maskref.pooled_proxies(q, k, bt.page_table, bt.cu_seqlens, bt.k_pool.shape[1])
-    ref_sc = np.full((bt.total_qblocks, bt.k_pool.shape[1], bt.max_pages), np.nan)
+    ref_sc = np.full((bt.total_qblocks, bt.k_pool.shape[1], bt.max_blocks), np.nan)
     for s, (qbar, kbar) in enumerate(prox):
         base = bt.cu_qblocks[s]
         for g in range(bt.k_pool.shape[1]):

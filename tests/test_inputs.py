@@ -45,3 +45,20 @@ def test_structured_planting_is_visible_in_logits():
     sal = set(bt.salient_pages[0][0].tolist()) | {0}
     others = [j for j in range(36) if j not in sal]                 # exclude the local window 36..39
     assert min(page_mean[j] for j in sal) > max(page_mean[j] for j in others)
+
+
+@pytest.mark.parametrize("bp", [16, 32])
+def test_repage_is_a_storage_change_only(bp):
+    from oracle import paging
+    wl = inputs.small_workload("rp", [64 * 6 + 17, 64 * 2, 5], 4, 2, generator="structured", seed=3, pool="shuffled")
+    bt = inputs.generate(wl)
+    rp = inputs.repage(bt, bp, 11)
+    assert rp.k_pool.shape[2] == bp and rp.max_blocks == bt.max_blocks
+    kl, vl, ptl = paging.logical_view(rp.k_pool, rp.v_pool, rp.page_table, rp.cu_seqlens, bp)
+    k0, v0, pt0 = paging.logical_view(bt.k_pool, bt.v_pool, bt.page_table, bt.cu_seqlens, 64)
+    np.testing.assert_array_equal(ptl, pt0)
+    np.testing.assert_array_equal(kl, k0)
+    np.testing.assert_array_equal(vl, v0)
+    # every physical page is used at most once
+    used = rp.page_table[rp.page_table >= 0]
+    assert used.size == np.unique(used).size
