@@ -22,12 +22,14 @@
 //   the B operand (bf16); V^T comes from the row-major V tile through
 //   ds_read_b64_tr_b16 (transposing LDS read);
 // * K and V page tiles are gathered with global_load_lds_dwordx4 (direct to LDS,
-//   no VGPR staging) into a ring of kRing page slots, kRing-1 visits ahead;
-// * one workgroup barrier per visit, between a page's key side (S^T, row max,
-//   partial vote) and its value side, is the only inter-wave synchronisation: it
-//   publishes both halves' vote margins, certifies that every wave is done with
-//   the previous page (so its slot can be refilled) and, with each wave's wait
-//   for its own gathers before it, that the next page is resident;
+//   no VGPR staging) into separate rings of kRing tile slots each;
+// * the pages are taken two at a time: the key sides of pages 2k and 2k+1 (S^T,
+//   row max, partial vote), one workgroup barrier, then their value sides.  The
+//   barrier is the only inter-wave synchronisation: it publishes both halves'
+//   vote margins, certifies that every wave is done with the K tiles of pages 2k,
+//   2k+1 and the V tiles of pages 2k-2, 2k-1 (so those slots can be refilled)
+//   and, with each wave's wait for its own gathers before it, that the K tiles of
+//   pages 2k+2, 2k+3 and the V tiles of pages 2k, 2k+1 are resident;
 // * the visit list of a unit (mask row -> validity -> page table -> physical
 //   page, first occurrence of a repeated id only) is resolved in LDS windows of
 //   512 entries before the visits, so the hot loop does no dependent global loads;
@@ -115,14 +117,6 @@ __device__ __forceinline__ void dma_16B_saddr(const void* sbase, uint32_t voff, 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N > 63 ? 63 : N) : "memory");
-}
-// wait until at most `pages` pages' worth of this wave's gather instructions are outstanding
-template <int PW>
-__device__ __forceinline__ void wait_pages_outstanding(int pages) {
-  if (pages <= 0) wait_vmcnt<0>();
-  else if (pages == 1) wait_vmcnt<PW>();
-  else if (pages == 2) wait_vmcnt<2 * PW>();
-  else wait_vmcnt<3 * PW>();
 }
 
 // Workgroup barrier for LDS hand-offs: this wave's LDS accesses complete first;
@@ -614,30 +608,31 @@ __device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
 // ---------------------------------------------------------------------------
 // ring kernel: HW = 4, 2 or 1 q heads of one KV head's group per workgroup
 // ---------------------------------------------------------------------------
-// Two waves per head (32 rows each).  K and V page tiles share one ring of kRing
-// page slots; each page is gathered kRing-1 visits ahead by waves 0 .. GW-1 (with
-// eight waves, one per SIMD: the gather instructions of a page queue at the CU's
-// load path for ~500 cycles, and meanwhile the other wave of each SIMD runs its
-// value side alone, which staggers the two).
-// Visit v: S^T of page v and the 32-row partial vote margin (written to LDS);
-// this wave's wait for its share of page v+1; a workgroup barrier; then the
-// gather of page v+3 into the slot of page v-1 (every wave finished page v-1
-// before the barrier), the block vote from both halves' margins, and the value
-// side of page v unless it is skipped.  Every wave runs the same number of
-// barriers (the visit count is workgroup-uniform), so no wait can hang.
+// Two waves per head (32 rows each).  K tiles and V tiles have rings of kRing slots
+// each; tiles are gathered by waves 0 .. GW-1 (with eight waves, one per SIMD: a
+// page's gather instructions queue at the CU's load path for hundreds of cycles,
+// and meanwhile the other wave of each SIMD runs its value side alone, which
+// staggers the two).
+// Step k (pages 2k, 2k+1): S^T of both pages and their 32-row partial vote margins
+// (written to LDS); this wave's wait for all its outstanding gathers; a workgroup
+// barrier; then the gathers of the K tiles of pages 2k+4, 2k+5 (into the K slots
+// of pages 2k, 2k+1) and the V tiles of pages 2k+2, 2k+3 (into the V slots of
+// pages 2k-2, 2k-1), and for each page in order the block vote from both halves'
+// margins and its value side unless it is skipped.  Every page's arithmetic is
+// exactly that of visiting the pages one at a time.  Every wave runs the same
+// number of barriers (the visit count is workgroup-uniform), so no wait can hang.
 template <int HW, int SUB>
 __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const PrefillArgs a, int heads_per_group,
                                                                     int nsub) {
   constexpr int NW = 2 * HW;   // waves
   constexpr int NT = 64 * NW;  // threads
   constexpr int GW = NW >= 4 ? NW / 2 : NW;  // waves that gather pages (waves 0 .. GW-1)
-  constexpr int PW = 32 / GW;                 // page-gather instructions per gathering wave per page
   constexpr int kWindow = window_len<SUB>();  // SUB: physical pages per logical block
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
   __shared__ WindowLds<SUB> wlds;
   __shared__ uint8_t dec_lds[HW][kWindow];
   __shared__ float mar_lds[HW][kWindow];
-  __shared__ float vote_val[HW][2][2];
+  __shared__ float vote_val[HW][2][2][2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
@@ -681,86 +676,93 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
     const int nv = resolve_window<NT, SUB>(a, u, mrow, k0, wl, wlds, wave, lane);
-    // this wave's share of visit p's K and V tiles (phys: the block's physical pages)
-    auto gather_tiles = [&](int jp, const int (&phys)[SUB], int p) {
-      const uint32_t slot = ring_addr + (uint32_t)(p % kRing) * kPageBytes;
-      const int valid_rows = u.L - jp * kPage;
-      const uint16_t* kb_sub[SUB];
-      const uint16_t* vb_sub[SUB];
-#pragma unroll
-      for (int x = 0; x < SUB; ++x) {
-        const int64_t off = (int64_t)phys[x] * a.kv_sp;
-        kb_sub[x] = kbase + off;
-        vb_sub[x] = vbase + off;
-      }
-      tg.template issue<SUB>(kb_sub, a.page_len, slot, valid_rows, false, wave, lane);
-      tg.template issue<SUB>(vb_sub, a.page_len, slot + kTileBytes, valid_rows, true, wave, lane);
-    };
-    auto gather = [&](int p) {
-      if (!gatherer) return;
+    // K tiles live in slots 0..3 of the first half of the ring, V tiles in the second
+    // half; page p uses K slot p % 4 and V slot p % 4.
+    auto k_slot = [&](int p) { return ring_addr + (uint32_t)(p % kRing) * kTileBytes; };
+    auto v_slot = [&](int p) { return ring_addr + (uint32_t)(kRing * kTileBytes) + (uint32_t)(p % kRing) * kTileBytes; };
+    // this wave's share of page p's K (is_v false) or V tile
+    auto gather_tile = [&](int p, bool is_v) {
+      if (!gatherer || p >= nv) return;
       const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]);
-      int phys[SUB];
+      const uint16_t* sub_base[SUB];
 #pragma unroll
-      for (int x = 0; x < SUB; ++x) phys[x] = __builtin_amdgcn_readfirstlane(wlds.vis_phys[p * SUB + x]);
-      gather_tiles(jp, phys, p);
+      for (int x = 0; x < SUB; ++x)
+        sub_base[x] = (is_v ? vbase : kbase) +
+                      (int64_t)__builtin_amdgcn_readfirstlane(wlds.vis_phys[p * SUB + x]) * a.kv_sp;
+      tg.template issue<SUB>(sub_base, a.page_len, is_v ? v_slot(p) : k_slot(p), u.L - jp * kPage, is_v, wave,
+                             lane);
     };
 
-    // ---- prologue: gather pages 0 .. kRing-2; page 0 resident before the first QK
-    const int pro = min(kRing - 1, nv);
-    for (int p = 0; p < pro; ++p) gather(p);
+    // ---- prologue: K of pages 0, 1 resident before the first QK; then V of pages 0, 1
+    //      and K of pages 2, 3 in flight (they land before the first step's barrier)
+    gather_tile(0, false);
+    gather_tile(1, false);
     if (nv > 0) {
-      wait_pages_outstanding<PW>(pro - 1);
+      wait_vmcnt<0>();
       lds_barrier();
     }
+    gather_tile(0, true);
+    gather_tile(1, true);
+    gather_tile(2, false);
+    gather_tile(3, false);
 
-    for (int v = 0; v < nv; ++v) {
-      const int slot = v % kRing;
-      // page v+3's table entries, read ahead of the QK so the gather after the barrier
-      // does not wait on LDS (index clamped inside the window when there is no such page)
-      const int pg = min(v + kRing - 1, kWindow - 1);
-      const int pg_j = wlds.vis_j[pg];
-      int pg_phys[SUB];
-#pragma unroll
-      for (int x = 0; x < SUB; ++x) pg_phys[x] = wlds.vis_phys[pg * SUB + x];
-      const int j = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
-      const uint32_t kb = ring_addr + (uint32_t)slot * kPageBytes;
-      const uint32_t vb = kb + kTileBytes;
-
-      f32x16_t acc[2];
-      qk_tile(kb, qf, lane, acc);
-      // ---- running-max update and block vote (Eq. (1), (2), (5))
-      const float mloc2 = mask_rowmax2(acc, j, u.i, r_blk, u.L, lane >> 5, scale_log2);
-      const float mnew2 = fmaxf(m2, mloc2);
-      const float dd = (row_ok && mloc2 != -INFINITY) ? (mloc2 - mnew2) : -INFINITY;
-      const float my_margin = max_lanes32(dd);
-      const bool vote = skip_on || logging;
-      const int par = v & 1;
-      if (vote && lane == 0) vote_val[hl][half][par] = my_margin;
-      // this wave's share of page v+1 has landed (page v+2's may still be in flight)
-      if (v + 1 < nv) wait_pages_outstanding<PW>(v + 2 < nv ? 1 : 0);
-      // one barrier per visit: past it, every wave has finished page v-1 (its slot is
-      // free), page v+1 is resident, and both halves' margins for page v are visible
+    // Step k: the key sides of pages 2k and 2k+1, one barrier, their value sides.
+    const bool vote = skip_on || logging;
+    for (int v = 0; v < nv; v += 2) {
+      const bool has_b = v + 1 < nv;
+      const int par = (v >> 1) & 1;
+      // ---- key sides (Eq. (1), (2), (5)): S^T, running max, partial margins
+      const int ja = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      f32x16_t acc_a[2], acc_b[2];
+      qk_tile(k_slot(v), qf, lane, acc_a);
+      const float mloc_a = mask_rowmax2(acc_a, ja, u.i, r_blk, u.L, lane >> 5, scale_log2);
+      const float mnew_a = fmaxf(m2, mloc_a);
+      const float dd_a = (row_ok && mloc_a != -INFINITY) ? (mloc_a - mnew_a) : -INFINITY;
+      const float marg_a = max_lanes32(dd_a);
+      float mnew_b = mnew_a, marg_b = -INFINITY;
+      if (has_b) {
+        const int jb = __builtin_amdgcn_readfirstlane(wlds.vis_j[v + 1]);
+        qk_tile(k_slot(v + 1), qf, lane, acc_b);
+        const float mloc_b = mask_rowmax2(acc_b, jb, u.i, r_blk, u.L, lane >> 5, scale_log2);
+        mnew_b = fmaxf(mnew_a, mloc_b);
+        const float dd_b = (row_ok && mloc_b != -INFINITY) ? (mloc_b - mnew_b) : -INFINITY;
+        marg_b = max_lanes32(dd_b);
+      }
+      if (vote && lane == 0) {
+        vote_val[hl][half][par][0] = marg_a;
+        vote_val[hl][half][par][1] = marg_b;
+      }
+      // every gather issued since the last barrier (K of pages 2k+2, 2k+3; V of pages
+      // 2k, 2k+1) has landed for this wave
+      wait_vmcnt<0>();
+      // one barrier per two pages: past it, the K tiles of pages 2k, 2k+1 and the V tiles
+      // of pages 2k-2, 2k-1 are free, the next pages' K and these pages' V are resident,
+      // and both halves' margins are visible
       lds_barrier();
-      const float partner = vote ? vote_val[hl][half ^ 1][par] : -INFINITY;
-      if (gatherer && v + kRing - 1 < nv) {
-        int phys[SUB];
-#pragma unroll
-        for (int x = 0; x < SUB; ++x) phys[x] = __builtin_amdgcn_readfirstlane(pg_phys[x]);
-        gather_tiles(__builtin_amdgcn_readfirstlane(pg_j), phys, v + kRing - 1);
-      }
-      const float margin2 = fmaxf(my_margin, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(partner))));
-      const bool skip = skip_on && (margin2 < tau2);
-      if (logging && half == 0 && lane == 0) {
-        dec_lds[hl][wlds.vis_k[v] - k0] = skip ? 1 : 0;
-        mar_lds[hl][wlds.vis_k[v] - k0] = margin2 * kLn2;
-      }
-      m2 = mnew2;
-      if (!skip) {
-        maybe_rebase(m2, b2, l2, o);
-        bf16x8_t pb[4];
-        l2 += permlane32_sum(probs_tile(acc, scale_log2, b2, pb));
-        pv_tile(vb, pb, lane, o);
-      }
+      const float pa = vote ? vote_val[hl][half ^ 1][par][0] : -INFINITY;
+      const float pbv = vote ? vote_val[hl][half ^ 1][par][1] : -INFINITY;
+      gather_tile(v + 4, false);
+      gather_tile(v + 5, false);
+      gather_tile(v + 2, true);
+      gather_tile(v + 3, true);
+      // ---- value side of page 2k, then of page 2k+1
+      auto value_side = [&](int w, const f32x16_t (&acc)[2], float mnew, float marg, float partner) {
+        const float margin2 = fmaxf(marg, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(partner))));
+        const bool skip = skip_on && (margin2 < tau2);
+        if (logging && half == 0 && lane == 0) {
+          dec_lds[hl][wlds.vis_k[w] - k0] = skip ? 1 : 0;
+          mar_lds[hl][wlds.vis_k[w] - k0] = margin2 * kLn2;
+        }
+        m2 = mnew;
+        if (!skip) {
+          maybe_rebase(m2, b2, l2, o);
+          bf16x8_t pb[4];
+          l2 += permlane32_sum(probs_tile(acc, scale_log2, b2, pb));
+          pv_tile(v_slot(w), pb, lane, o);
+        }
+      };
+      value_side(v, acc_a, mnew_a, marg_a, pa);
+      if (has_b) value_side(v + 1, acc_b, mnew_b, marg_b, pbv);
     }
     wait_vmcnt<0>();  // no page gather may still be writing LDS past this point
     __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
