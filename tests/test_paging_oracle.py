@@ -86,3 +86,30 @@ def test_unusable_physical_page_invalidates_its_block():
     pt64b[0, 2] = -1
     b = osk.osk_reference(q, k64, v64, pt64b, cu, om, ml, delta=-1.0)
     np.testing.assert_array_equal(np.nan_to_num(np.asarray(a["out"]), nan=-3.0), np.nan_to_num(np.asarray(b["out"]), nan=-3.0))
+
+
+def test_128_token_blocks_match_brute_force_and_repaging():
+    # CoSA Appendix D.1: b = 128 logical blocks over b_p = 64 (and 16) token pages.  The
+    # oracle takes the block as its page size on the logical view; without skipping it
+    # must equal per-token softmax over the support set, and the view must not depend
+    # on how the tokens are paged.
+    lens = [64 * 7 + 30, 64 * 4, 100]
+    q, k64, v64, pt64, cu = case(lens, 4, 2, 19)
+    kl, vl, ptl = paging.logical_view(k64, v64, pt64, cu, 64, block=128)
+    assert kl.shape[2] == 128 and ptl.shape[1] == -(-max(lens) // 128)
+    om, ml = osk.full_causal_mask(cu, 2, page_size=128)
+    out_bf, lse_bf = osk.brute_force_attention(q, kl, vl, ptl, cu, om, ml, page_size=128)
+    res = osk.osk_reference(q, kl, vl, ptl, cu, om, ml, delta=-1, page_size=128)
+    np.testing.assert_allclose(res["out"], out_bf, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse_bf, atol=1e-12)
+    # the same tokens in 16-token pages give the same 128-token view
+    kp, vp, pt = repage(k64, v64, pt64, lens, 16, 3)
+    kl2, vl2, ptl2 = paging.logical_view(kp, vp, pt, cu, 16, block=128)
+    np.testing.assert_array_equal(ptl, ptl2)
+    np.testing.assert_array_equal(kl, kl2)
+    # with skipping, the 128-row vote: the builders and the oracle run at page_size 128
+    om2, ml2 = maskref.build_order_mask(q, kl, ptl, cu, 2, 0.5, page_size=128)
+    r2 = osk.osk_reference(q, kl, vl, ptl, cu, om2, ml2, delta=float(np.exp(-0.05) * max(lens)), page_size=128)
+    assert np.isfinite(r2["out"]).all()
+    km = kap.build_kap_mask(q, kl, ptl, cu, 2, 16, kap.MODE_FRACTION, 0.5, page_size=128)
+    assert km[0].shape[0] == sum(-(-L // 128) for L in lens)
