@@ -10,8 +10,9 @@ dense causal mask and skipping off (the dense baseline), and the mask builder.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 Prints one JSON line.  value = effective TFLOP/s on the visited blocks:
-QK^T flops of every visited (q head, page) plus P V flops of the computed ones,
-each 2*64*64*128, over the median call time.
+QK^T flops of every visited (q head, block) plus P V flops of the computed ones,
+each 2*b*b*128 for b-token logical blocks (b = 64, or 128 for the *_b128
+workload), over the median call time.
 """
 import argparse
 import hashlib
@@ -30,6 +31,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TILE_FLOP = 2 * 64 * 64 * 128  # one 64x64x128 contraction
+
+
+def block_flop(block_size: int) -> float:
+    """One b x b x 128 contraction (QK^T or P V of one visited (q head, block))."""
+    return TILE_FLOP * (block_size // 64) ** 2
 KAP_STRIDE = 16
 KERNEL_SOURCES = ["block_sparse_long_osk_amd/csrc/osk_prefill.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "osk_prefill_cfg4_128k_traffic.json")
@@ -121,11 +127,15 @@ def cpu_baseline(batch, wl, delta, budget_s=15.0):
         blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         blas_threads = 1
+    from oracle import paging
     q = inputs.bf16_bits_to_f32(batch.q)
     k = inputs.bf16_bits_to_f32(batch.k_pool)
     v = inputs.bf16_bits_to_f32(batch.v_pool)
+    B, pt = batch.block_size, batch.page_table
+    if k.shape[2] != B:   # the oracle's pools at the logical block size
+        k, v, pt = paging.logical_view(k, v, pt, batch.cu_seqlens, k.shape[2], block=B)
     t_mask = time.perf_counter()
-    om, ml = maskref.build_order_mask(q, k, batch.page_table, batch.cu_seqlens, wl.num_kv_heads, wl.budget1)
+    om, ml = maskref.build_order_mask(q, k, pt, batch.cu_seqlens, wl.num_kv_heads, wl.budget1, page_size=B)
     t_mask = time.perf_counter() - t_mask
     rng = np.random.default_rng(0)
     order = rng.permutation(batch.total_qblocks)
@@ -135,10 +145,10 @@ def cpu_baseline(batch, wl, delta, budget_s=15.0):
     for qb in order:
         units = [(int(qb), g) for g in range(wl.num_kv_heads)]
         t = time.perf_counter()
-        res = osk.osk_reference(q, k, v, batch.page_table, batch.cu_seqlens, om, ml, delta, units=units)
+        res = osk.osk_reference(q, k, v, pt, batch.cu_seqlens, om, ml, delta, page_size=B, units=units)
         spent += time.perf_counter() - t
         d = res["decisions"][qb]
-        flops += TILE_FLOP * (float((d != 2).sum()) + float((d == 0).sum()))
+        flops += block_flop(B) * (float((d != 2).sum()) + float((d == 0).sum()))
         n_blocks += 1
         if spent >= budget_s:
             break
@@ -246,7 +256,7 @@ def main():
                        device="cuda")
     builder_ms, _ = time_calls(lambda: runner.build_mask(db, wl.budget1, workspace=ws_b), 5, 2)
     kap_ms = None
-    if db.num_q_heads // db.num_kv_heads * (64 // KAP_STRIDE) <= 32:
+    if db.num_q_heads // db.num_kv_heads * (db.block_size // KAP_STRIDE) <= 32:
         # the KAP builder (CoSA section 4.2): stride 16, fixed fraction = the workload's budget, and Top-p 0.95
         kw = binding.cosa_kap_mask_width(db.max_blocks, binding.COSA_KAP_TOP_P, 0.95)
         ws_k = torch.empty(binding.cosa_build_kap_mask_workspace_bytes(db.dims(kw)), dtype=torch.uint8, device="cuda")
@@ -264,7 +274,8 @@ def main():
     visited = int((dec != 2).sum().item())
     computed = int((dec == 0).sum().item())
     del logged, dec
-    flop = TILE_FLOP * (visited + computed)
+    B = db.block_size
+    flop = block_flop(B) * (visited + computed)
 
     # ---- timed OSK calls (no logging)
     outs = runner.allocate_outputs(db, width, log=False)
@@ -285,7 +296,7 @@ def main():
     if not args.no_dense:
         dom, dml = runner.dense_mask(db)
         d_visited = int(dml.sum().item()) * (db.num_q_heads // db.num_kv_heads)
-        d_flop = 2 * TILE_FLOP * d_visited
+        d_flop = 2 * block_flop(B) * d_visited
         douts = runner.allocate_outputs(db, dom.shape[2], log=False)
         douts.lse = None
         dws = runner.workspace_for(db, dom.shape[2])
@@ -311,11 +322,12 @@ def main():
             tr = json.load(f)
         if tr.get("workload") == wl.name and tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
-    kv_bytes = 2 * 64 * 128 * 2 * (visited // (db.num_q_heads // db.num_kv_heads))
+    kv_bytes = 2 * B * 128 * 2 * (visited // (db.num_q_heads // db.num_kv_heads))
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "frac_of_attainable": tflops / attain["mfma_bf16_tflops"],
-                "kernel": "osk_prefill_ring_kernel<4> (+ schedule kernel, 0.3% of the call)",
+                "kernel": ("osk_prefill_ring_kernel<4>" if B == 64 else "osk_prefill_b128_kernel<2>")
+                          + " (+ schedule kernel, 0.3% of the call)",
                 "algorithmic_flop_per_launch": flop,
                 "kv_gather_gbs": kv_bytes / (med * 1e-3) / 1e9,
                 "kv_gather_frac_of_hbm": kv_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -335,7 +347,8 @@ def main():
         "data": "synthetic (seeded structured generator; no dataset or model weights)",
         "config": {"workload": wl.name, "seq_len": wl.seq_lens[0] if len(wl.seq_lens) == 1 else list(wl.seq_lens),
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": 128,
-                   "page_size": 64, "budget1": wl.budget1, "skip_scale_delta": delta},
+                   "page_size": int(batch.k_pool.shape[2]), "block_size": B, "budget1": wl.budget1,
+                   "skip_scale_delta": delta},
         "visited_q_head_pages": n_q_visits, "computed_q_head_pages": computed,
         "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
         "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,

@@ -26,7 +26,7 @@ class CosaOskDims(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("total_q_tokens", ctypes.c_int32),
         ("total_qblocks", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
         ("num_phys_pages", ctypes.c_int32), ("max_mask_len", ctypes.c_int32),
-        ("sm_scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("block_size", ctypes.c_int32),
         ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
         ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
         ("kv_stride_page", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64), ("kv_stride_tok", ctypes.c_int64),
@@ -107,16 +107,16 @@ def _check(status: int, where: str):
 # dims
 # ----------------------------------------------------------------------------
 def make_dims(q, k_pool, page_table, total_qblocks: int, max_mask_len: int, out=None,
-              sm_scale: float = 0.0) -> CosaOskDims:
-    """Dims from tensor shapes/strides: q, out [T, Hq, 128]; pools [n_phys, Hkv, 64, 128];
-    page_table [S, max_pages]."""
+              sm_scale: float = 0.0, block_size: int = 64) -> CosaOskDims:
+    """Dims from tensor shapes/strides: q, out [T, Hq, 128]; pools [n_phys, Hkv, page_size, 128];
+    page_table [S, max_pages]; logical blocks of block_size (64 or 128) tokens."""
     T, Hq, d = q.shape
     n_phys, Hkv, P, d2 = k_pool.shape
     out = q if out is None else out
     return CosaOskDims(
         num_seqs=page_table.shape[0], num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, page_size=P,
         total_q_tokens=T, total_qblocks=int(total_qblocks), max_pages_per_seq=page_table.shape[1],
-        num_phys_pages=n_phys, max_mask_len=int(max_mask_len), sm_scale=float(sm_scale), reserved=0,
+        num_phys_pages=n_phys, max_mask_len=int(max_mask_len), sm_scale=float(sm_scale), block_size=int(block_size),
         q_stride_tok=q.stride(0), q_stride_head=q.stride(1), o_stride_tok=out.stride(0),
         o_stride_head=out.stride(1), kv_stride_page=k_pool.stride(0), kv_stride_head=k_pool.stride(1),
         kv_stride_tok=k_pool.stride(2))

@@ -20,26 +20,33 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool stride_ok(int64_t s) { return s > 0 && (s % 8) == 0; }
 
-// logical 64-token blocks a page-table row can address
+// tokens per logical block (0 selects 64)
+int32_t block_of(const cosa_osk_dims_t* d) { return d->block_size == 0 ? kPage : d->block_size; }
+
+// logical blocks a page-table row can address
 int32_t max_blocks(const cosa_osk_dims_t* d) {
-  return (int32_t)(((int64_t)d->max_pages_per_seq * d->page_size + kPage - 1) / kPage);
+  const int64_t b = block_of(d);
+  return (int32_t)(((int64_t)d->max_pages_per_seq * d->page_size + b - 1) / b);
 }
 
 cosa_status_t check_dims(const cosa_osk_dims_t* d) {
   if (d == nullptr) return COSA_ERR_INVALID_ARG;
-  if (d->reserved != 0) return COSA_ERR_INVALID_ARG;
+  if (d->block_size != 0 && d->block_size != 64 && d->block_size != 128) return COSA_ERR_UNSUPPORTED;
   if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->total_q_tokens < 0 ||
       d->total_qblocks < 0 || d->max_pages_per_seq < 1 || d->num_phys_pages < 0 || d->max_mask_len < 0)
     return COSA_ERR_INVALID_ARG;
   if (d->head_dim != kHeadDim) return COSA_ERR_UNSUPPORTED;
-  // physical pages of 16, 32 or 64 tokens; the logical block is always 64 tokens
-  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return COSA_ERR_UNSUPPORTED;
+  // physical pages of 16, 32 or 64 tokens, or 128 under 128-token blocks: a page
+  // size that divides the logical block
+  const int32_t blk = block_of(d);
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64 && !(blk == 128 && d->page_size == 128))
+    return COSA_ERR_UNSUPPORTED;
   if (d->num_q_heads % d->num_kv_heads != 0) return COSA_ERR_UNSUPPORTED;
   if (d->total_qblocks > cosa_osk::kMaxQBlocks || d->max_mask_len > cosa_osk::kMaxMaskLen ||
       max_blocks(d) > cosa_osk::kMaxPagesPerSeq)
     return COSA_ERR_UNSUPPORTED;
-  // every query block holds 1..64 tokens
-  if ((int64_t)d->total_q_tokens > (int64_t)kPage * d->total_qblocks || d->total_qblocks > d->total_q_tokens)
+  // every query block holds 1..block tokens
+  if ((int64_t)d->total_q_tokens > (int64_t)blk * d->total_qblocks || d->total_qblocks > d->total_q_tokens)
     return COSA_ERR_INVALID_ARG;
   if (!stride_ok(d->q_stride_tok) || !stride_ok(d->q_stride_head) || !stride_ok(d->o_stride_tok) ||
       !stride_ok(d->o_stride_head) || !stride_ok(d->kv_stride_page) || !stride_ok(d->kv_stride_head) ||
@@ -139,6 +146,7 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   a.max_pages = max_blocks(dims);
   a.pt_stride = dims->max_pages_per_seq;
   a.page_len = dims->page_size;
+  a.block = block_of(dims);
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   a.sm_scale = resolved_scale(dims);
@@ -216,6 +224,7 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   a.max_pages = max_blocks(dims);
   a.pt_stride = dims->max_pages_per_seq;
   a.page_len = dims->page_size;
+  a.block = block_of(dims);
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   a.budget1 = budget1;
@@ -259,11 +268,14 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   if (mode != COSA_KAP_FRACTION && mode != COSA_KAP_TOP_P) return COSA_ERR_INVALID_ARG;
   if (mode == COSA_KAP_FRACTION ? !(budget > 0.f && budget <= 1.f) : !(budget >= 0.f && budget <= 1.f))
     return COSA_ERR_INVALID_ARG;
-  if (stride != 8 && stride != 16) return COSA_ERR_UNSUPPORTED;
+  // 4 or 8 samples per logical block: strides 16 and 8 for 64-token blocks, 32 and 16
+  // for 128-token blocks
+  const int blk = block_of(dims);
+  if (stride <= 0 || (stride * 4 != blk && stride * 8 != blk)) return COSA_ERR_UNSUPPORTED;
   const int G = dims->num_q_heads / dims->num_kv_heads;
   // the sampled rows of a query block (all heads of the group) form a power-of-two group
   // of at most 32 MFMA columns
-  const int rb = G * (cosa_osk::kPage / stride);
+  const int rb = G * (blk / stride);
   if (rb > 32 || (rb & (rb - 1)) != 0) return COSA_ERR_UNSUPPORTED;
   if (dims->max_mask_len < cosa_kap_mask_width(max_blocks(dims), mode, budget)) return COSA_ERR_INVALID_ARG;
   const size_t need = cosa_build_kap_mask_workspace_bytes(dims);
@@ -293,6 +305,7 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   a.max_pages = max_blocks(dims);
   a.pt_stride = dims->max_pages_per_seq;
   a.page_len = dims->page_size;
+  a.block = block_of(dims);
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   a.stride = stride;
@@ -324,6 +337,7 @@ cosa_status_t cosa_validate_order_mask(const cosa_osk_dims_t* dims, const int32_
   a.max_pages = max_blocks(dims);
   a.pt_stride = dims->max_pages_per_seq;
   a.page_len = dims->page_size;
+  a.block = block_of(dims);
   a.num_phys = dims->num_phys_pages;
   a.max_mask_len = dims->max_mask_len;
   return cosa_osk::launch_validate(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;

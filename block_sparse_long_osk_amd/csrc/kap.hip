@@ -14,7 +14,7 @@
 //
 // Kernels:
 //   kap_score  one wave per KV head and BPW consecutive query blocks of a
-//              sequence; their G heads x (64/stride) sampled rows per block fill
+//              sequence; their G heads x (block/stride) sampled rows per block fill
 //              the 32 columns of S^T = K~ Q~^T tiles (v_mfma_f32_32x32x16_bf16,
 //              32 sampled keys per tile, read through the page table).  Pass 1:
 //              row maxima; pass 2: the same logits again (bitwise the same), block
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void kap_select_kernel(const KapArgs a, int ca
 hipError_t launch_build_kap_mask(const KapArgs& a, hipStream_t stream) {
   if (a.total_qblocks == 0) return hipSuccess;
   const int G = a.hq / a.hkv;
-  const int per = kPage / a.stride;
+  const int per = a.block / a.stride;  // sampled rows and keys per logical block: 4 or 8
   const int bpw = 32 / (G * per) * kKapColumnTiles;  // query blocks per wave
   const dim3 sgrid((unsigned)(a.total_qblocks / bpw + a.num_seqs), (unsigned)a.hkv);
   if (per == 4)

@@ -9,7 +9,8 @@
 //
 // Kernels:
 //   pool   one workgroup per (query block, KV head):
-//          qbar = sum_h mean_r q, kbar = mean_t k of the same-index logical page;
+//          qbar = sum_h mean_r q, kbar = mean_t k of the same-index logical block
+//          (64 or 128 tokens);
 //          Q and K are each read once in 16-byte chunks along the head dimension.
 //   score  one workgroup per 8 consecutive query blocks of a sequence and a KV
 //          head: fp32 scores of the causal pages, each pooled key row read once
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
   const int i = qb - a.cu_qblocks[s];
   const int tok0 = a.cu_seqlens[s];
   const int L = a.cu_seqlens[s + 1] - tok0;
-  const int rows = min(kPage, L - i * kPage);
+  const int rows = min(a.block, L - i * a.block);
   const int G = a.hq / a.hkv;
   auto add8 = [](float (&acc)[8], const uint16_t* p) {
     const uint4 w = *(const uint4*)p;
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int hh = 0; hh < G; ++hh) {
     const uint16_t* qh = a.q + (int64_t)tok0 * a.q_st + (int64_t)(g * G + hh) * a.q_sh + chunk * 8;
-    for (int r = rg; r < rows; r += 16) add8(acc, qh + (int64_t)(i * kPage + r) * a.q_st);
+    for (int r = rg; r < rows; r += 16) add8(acc, qh + (int64_t)(i * a.block + r) * a.q_st);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rg][chunk * 8 + e] = acc[e];
@@ -74,8 +75,8 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
   __syncthreads();
   // ---- kbar: mean of the same-index logical block's keys (through its physical pages)
   const int32_t* pt_row = a.page_table + (int64_t)s * a.pt_stride;
-  int ph[4] = {-1, -1, -1, -1};
-  const bool has_page = i < a.max_pages && block_phys(pt_row, a.pt_stride, i, L, a.page_len, a.num_phys, ph);
+  int ph[kMaxBlockPages];
+  const bool has_page = i < a.max_pages && block_phys(pt_row, a.pt_stride, i, L, a.page_len, a.block, a.num_phys, ph);
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   if (has_page) {
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(64) void validate_kernel(const ValidateArgs a) {
   const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
   const int i = qb - a.cu_qblocks[s];
   const int L = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
-  const int n_pages = min((L + kPage - 1) / kPage, a.max_pages);
+  const int n_pages = min((L + a.block - 1) / a.block, a.max_pages);
   int len = a.mask_len[(int64_t)qb * a.hkv + g];
   int c_range = 0, c_causal = 0, c_dup = 0, c_len = 0, c_phys = 0;
   if (len < 0 || len > a.max_mask_len) {
@@ -269,8 +270,9 @@ __global__ __launch_bounds__(64) void validate_kernel(const ValidateArgs a) {
     if (id > i) ++c_causal;
     const uint32_t bit = 1u << (id & 31);
     if (atomicOr(&seen[id >> 5], bit) & bit) ++c_dup;
-    int ph[4];
-    if (!block_phys(a.page_table + (int64_t)s * a.pt_stride, a.pt_stride, id, L, a.page_len, a.num_phys, ph))
+    int ph[kMaxBlockPages];
+    if (!block_phys(a.page_table + (int64_t)s * a.pt_stride, a.pt_stride, id, L, a.page_len, a.block, a.num_phys,
+                    ph))
       ++c_phys;
   }
   // reduce over the wave, one atomic per counter

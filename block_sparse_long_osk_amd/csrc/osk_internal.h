@@ -6,12 +6,16 @@
 
 namespace cosa_osk {
 
-// kPage: the logical block (query block and key block) of the method, 64 tokens.  The
-// KV cache's physical pages hold page_len = 16, 32 or 64 tokens; logical block j of a
-// sequence is its tokens 64 j .. 64 j + 63, token t stored in the physical page of
-// page-table entry t / page_len at row t % page_len.  max_pages in the argument blocks
-// below counts logical blocks per sequence; pt_stride is the page-table row length.
+// Blocks, tiles and pages.  The logical block (query block, key block, unit of a skip
+// vote) holds `block` = 64 or 128 tokens; the KV cache's physical pages hold page_len =
+// 16, 32, 64 (or 128, for 128-token blocks) tokens.  Logical block j of a sequence is
+// its tokens block*j .. block*j + block - 1, token t stored in the physical page of
+// page-table entry t / page_len at row t % page_len.  kPage is the height of one K or
+// V tile in LDS, 64 tokens: a 64-token block is one tile, a 128-token block two.
+// max_pages in the argument blocks below counts logical blocks per sequence; pt_stride
+// is the page-table row length.
 constexpr int kPage = 64;
+constexpr int kMaxBlockPages = 8;        // physical pages of one logical block (128 / 16)
 constexpr int kHeadDim = 128;
 constexpr int kMaxQBlocks = 16384;       // schedule keys live in LDS
 constexpr int kMaxMaskLen = 8191;        // schedule histogram lives in LDS
@@ -35,7 +39,8 @@ struct PrefillArgs {
   int32_t* error_count;  // workspace health word (zeroed by the schedule kernel; 0 after every call)
   int64_t q_st, q_sh, o_st, o_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
-  int32_t pt_stride, page_len;  // page-table row length; tokens per physical page (16, 32 or 64)
+  int32_t pt_stride, page_len;  // page-table row length; tokens per physical page
+  int32_t block;                // tokens per logical block (64 or 128)
   float sm_scale;
   float delta;
 };
@@ -54,7 +59,7 @@ struct BuilderArgs {
   float* score_rows;  // [total_qblocks, hkv, max_pages]: scores, or workspace when scores is null
   int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
-  int32_t pt_stride, page_len;
+  int32_t pt_stride, page_len, block;
   float budget1;
   uint32_t flags;
 };
@@ -67,7 +72,7 @@ struct ValidateArgs {
   const int32_t* mask_len;
   int32_t* bad;
   int32_t num_seqs, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
-  int32_t pt_stride, page_len;
+  int32_t pt_stride, page_len, block;
 };
 
 struct KapArgs {
@@ -84,20 +89,20 @@ struct KapArgs {
   uint8_t* flag_rows;   // [total_qblocks, hkv, max_pages]: flags_out, or workspace
   int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
-  int32_t pt_stride, page_len;
+  int32_t pt_stride, page_len, block;
   int32_t stride, mode;
   float budget, sm_scale;
 };
 
 // Physical pages of logical block j of a sequence (pt_row: its page-table row, n_pt
 // entries): the block is usable iff every page holding one of its tokens t < L is a
-// valid page id; then ph[0 .. 64 / page_len - 1] are set (pages past L repeat ph[0]).
-__device__ __forceinline__ bool block_phys(const int32_t* pt_row, int n_pt, int j, int L, int page_len,
+// valid page id; then ph[0 .. block / page_len - 1] are set (pages past L repeat ph[0]).
+__device__ __forceinline__ bool block_phys(const int32_t* pt_row, int n_pt, int j, int L, int page_len, int block,
                                            int num_phys, int* ph) {
-  const int sub = kPage / page_len;
+  const int sub = block / page_len;
   bool ok = true;
   for (int s = 0; s < sub; ++s) {
-    const int t0 = j * kPage + s * page_len;
+    const int t0 = j * block + s * page_len;
     int p = -1;
     if (t0 < L) {
       const int e = j * sub + s;

@@ -57,10 +57,10 @@ typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
 constexpr int kTileBytes = kPage * kHeadDim * 2;  // one K or V page of one KV head: 16 KiB
 constexpr int kPageBytes = 2 * kTileBytes;        // K then V
-// mask entries resolved per window: 512, or 256 when a logical block spans several
-// physical pages (their ids take LDS)
-template <int SUB>
-constexpr int window_len() { return SUB == 1 ? 512 : 256; }
+// mask entries resolved per window: 512, or fewer when a logical block spans several
+// physical pages (NPB ids per entry take LDS)
+template <int NPB>
+constexpr int window_len() { return NPB == 1 ? 512 : NPB <= 4 ? 256 : 128; }
 constexpr int kRing = 4;                          // page slots in flight per workgroup
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -318,7 +318,7 @@ struct Unit {
   const int32_t* pt_row;
 };
 
-template <int HW>
+template <int HW, int B>
 __device__ __forceinline__ Unit decode_unit(const PrefillArgs& a, int heads_per_group, int nsub, int hl) {
   Unit u;
   const int per_qb = a.hkv * nsub;
@@ -338,17 +338,18 @@ __device__ __forceinline__ Unit decode_unit(const PrefillArgs& a, int heads_per_
   u.L = a.cu_seqlens[lo + 1] - u.tok0;
   // pages addressable through the page table (cu_seqlens and max_pages_per_seq agree
   // for well-formed inputs; the clamp keeps every table and bitmap access in bounds)
-  u.n_pages = min((u.L + kPage - 1) / kPage, a.max_pages);
+  u.n_pages = min((u.L + B - 1) / B, a.max_pages);
   u.len = min(max(a.mask_len[(int64_t)u.qb * a.hkv + u.g], 0), a.max_mask_len);
   u.pt_row = a.page_table + (int64_t)lo * a.pt_stride;
   return u;
 }
 
-// The wave's 32 query rows as MFMA B operands: lane holds row r_blk, dims
-// 16 c + 8 hi .. +8 (zero for rows past the sequence end).
+// The wave's 32 query rows as MFMA B operands: lane holds row r_blk of the B-token
+// query block, dims 16 c + 8 hi .. +8 (zero for rows past the sequence end).
+template <int B>
 __device__ __forceinline__ void load_q(const PrefillArgs& a, const Unit& u, int r_blk, bool row_ok, int hi,
                                        bf16x8_t (&qf)[8]) {
-  const uint16_t* qrow = a.q + (int64_t)(u.tok0 + u.i * kPage + r_blk) * a.q_st + (int64_t)u.h * a.q_sh + hi * 8;
+  const uint16_t* qrow = a.q + (int64_t)(u.tok0 + u.i * B + r_blk) * a.q_st + (int64_t)u.h * a.q_sh + hi * 8;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     i32x4_t x = {0, 0, 0, 0};
@@ -360,13 +361,13 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Unit& u, int 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
 }
 
-// Visit list of one window of the mask row, in LDS.
-template <int SUB>
+// Visit list of one window of the mask row, in LDS (NPB physical page ids per block).
+template <int NPB>
 struct WindowLds {
-  static constexpr int kWin = window_len<SUB>();
+  static constexpr int kWin = window_len<NPB>();
   int raw_id[kWin];
-  int raw_phys[kWin * SUB];  // physical pages of each entry's logical block
-  int vis_phys[kWin * SUB];
+  int raw_phys[kWin * NPB];  // physical pages of each entry's logical block
+  int vis_phys[kWin * NPB];
   int vis_j[kWin];
   int vis_k[kWin];
   uint32_t seen_bits[kMaxPagesPerSeq / 32];
@@ -377,26 +378,27 @@ struct WindowLds {
 // visited when its id is a causal logical block of the sequence (0 <= id <= i, id
 // below the block count) whose physical pages are valid, and only at its first
 // occurrence in the row (bitmap over the sequence's blocks, kept across windows).
+// B: tokens per logical block; NPB = B / page_len physical pages per block.
 // Returns the number of visits.  Called by every thread of the workgroup; ends with
 // a barrier.
-template <int NT, int SUB>
+template <int NT, int NPB, int B>
 __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& u, const int32_t* mrow, int k0,
-                                              int wl, WindowLds<SUB>& w, int wave, int lane) {
+                                              int wl, WindowLds<NPB>& w, int wave, int lane) {
   for (int e = threadIdx.x; e < wl; e += NT) {
     const int id = mrow[k0 + e];
-    int ph[SUB];
+    int ph[NPB];
     bool ok = false;
     if (id >= 0 && id < u.n_pages && id <= u.i) {
-      if (SUB == 1) {
+      if (NPB == 1) {
         ph[0] = u.pt_row[id];
         ok = ph[0] >= 0 && ph[0] < a.num_phys;
       } else {
-        ok = block_phys(u.pt_row, a.pt_stride, id, u.L, a.page_len, a.num_phys, ph);
+        ok = block_phys(u.pt_row, a.pt_stride, id, u.L, a.page_len, B, a.num_phys, ph);
       }
     }
     w.raw_id[e] = ok ? id : -1;
 #pragma unroll
-    for (int x = 0; x < SUB; ++x) w.raw_phys[e * SUB + x] = ok ? ph[x] : -1;
+    for (int x = 0; x < NPB; ++x) w.raw_phys[e * NPB + x] = ok ? ph[x] : -1;
   }
   __syncthreads();
   // wave 0 compacts the visited entries in mask order
@@ -424,7 +426,7 @@ __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& 
       if (keep) {
         const int p = count + __popcll(km & ((1ull << lane) - 1ull));
 #pragma unroll
-        for (int x = 0; x < SUB; ++x) w.vis_phys[p * SUB + x] = w.raw_phys[e * SUB + x];
+        for (int x = 0; x < NPB; ++x) w.vis_phys[p * NPB + x] = w.raw_phys[e * NPB + x];
         w.vis_j[p] = id;
         w.vis_k[p] = k0 + e;
       }
@@ -467,18 +469,23 @@ __device__ __forceinline__ void qk_tile(uint32_t kb, const bf16x8_t (&qf)[8], in
   for (int x = 0; x < 8; ++x) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-// Visibility on the diagonal and tail pages: t <= c and t < L.
-__device__ __forceinline__ void mask_tile(f32x16_t (&acc)[2], int j, int i, int r_blk, int L, int hi) {
-  if (j == i || L - j * kPage < kPage) {
-    const int c_tok = i * kPage + r_blk;
+// Visibility t <= c and t < L for the 64-key tile whose first key is token key0 of the
+// sequence, the lane's query row being token c_tok; `need` (wave-uniform) is false
+// when the tile is known to be wholly visible.
+__device__ __forceinline__ void mask_tile_at(f32x16_t (&acc)[2], int key0, int c_tok, int L, int hi, bool need) {
+  if (need) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int t = j * kPage + tt * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        const int t = key0 + tt * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
         if (t > c_tok || t >= L) acc[tt][e] = -INFINITY;
       }
   }
+}
+// 64-token blocks: masking is needed on the diagonal block and on the tail block.
+__device__ __forceinline__ void mask_tile(f32x16_t (&acc)[2], int j, int i, int r_blk, int L, int hi) {
+  mask_tile_at(acc, j * kPage, i * kPage + r_blk, L, hi, j == i || L - j * kPage < kPage);
 }
 // The page's local row max in the scaled log2 domain; lanes l and l^32 hold the
 // same row.
@@ -573,12 +580,14 @@ __device__ __forceinline__ void fill_log_tail(const PrefillArgs& a, const Unit& 
   }
 }
 
-// O <- O / l (0 when nothing was computed), bf16 out, natural-log LSE.
+// O <- O / l (0 when nothing was computed), bf16 out, natural-log LSE; row r_blk of a
+// B-token query block.
+template <int B>
 __device__ __forceinline__ void store_output(const PrefillArgs& a, const Unit& u, const f32x16_t (&o)[4], float l2,
                                              float b2, int r_blk, bool row_ok, int lane) {
   const int hi = lane >> 5;
   const float inv_l = l2 > 0.f ? 1.f / l2 : 0.f;
-  uint16_t* orow = a.out + (int64_t)(u.tok0 + u.i * kPage + r_blk) * a.o_st + (int64_t)u.h * a.o_sh;
+  uint16_t* orow = a.out + (int64_t)(u.tok0 + u.i * B + r_blk) * a.o_st + (int64_t)u.h * a.o_sh;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const f32x16_t ov = o[nt] * inv_l;
@@ -598,7 +607,7 @@ __device__ __forceinline__ void store_output(const PrefillArgs& a, const Unit& u
     }
   }
   if (a.lse != nullptr && hi == 0 && row_ok)
-    a.lse[(int64_t)(u.tok0 + u.i * kPage + r_blk) * a.hq + u.h] = l2 > 0.f ? (b2 + log2f(l2)) * kLn2 : -INFINITY;
+    a.lse[(int64_t)(u.tok0 + u.i * B + r_blk) * a.hq + u.h] = l2 > 0.f ? (b2 + log2f(l2)) * kLn2 : -INFINITY;
 }
 
 __device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
@@ -638,7 +647,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   const int half = wave & 1;  // rows 32*half .. +31 of the block; the halves of a head sit on different SIMDs
   const int hl = wave >> 1;   // head within the workgroup
-  const Unit u = decode_unit<HW>(a, heads_per_group, nsub, hl);
+  const Unit u = decode_unit<HW, kPage>(a, heads_per_group, nsub, hl);
   const bool skip_on = a.delta > 0.f;
   const float scale_log2 = a.sm_scale * kLog2e;
   const float tau2 = skip_threshold2(a, u.L);
@@ -649,7 +658,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
   const int r_blk = half * 32 + (lane & 31);
   const bool row_ok = (u.i * kPage + r_blk) < u.L;
   bf16x8_t qf[8];
-  load_q(a, u, r_blk, row_ok, lane >> 5, qf);
+  load_q<kPage>(a, u, r_blk, row_ok, lane >> 5, qf);
 
   // ---- online-softmax state (log2 domain, scaled).  m2: the running row max of Eq. (2),
   //      which the skip vote uses.  b2: the exponent base of l2 and O; it follows m2 lazily
@@ -675,7 +684,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     const int wl = min(kWindow, u.len - k0);
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
-    const int nv = resolve_window<NT, SUB>(a, u, mrow, k0, wl, wlds, wave, lane);
+    const int nv = resolve_window<NT, SUB, kPage>(a, u, mrow, k0, wl, wlds, wave, lane);
     // K tiles live in slots 0..3 of the first half of the ring, V tiles in the second
     // half; page p uses K slot p % 4 and V slot p % 4.
     auto k_slot = [&](int p) { return ring_addr + (uint32_t)(p % kRing) * kTileBytes; };
@@ -770,7 +779,174 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     __syncthreads();
   }
   if (logging && half == 0) fill_log_tail(a, u, lane);
-  store_output(a, u, o, l2, b2, r_blk, row_ok, lane);
+  store_output<kPage>(a, u, o, l2, b2, r_blk, row_ok, lane);
+}
+
+// ---------------------------------------------------------------------------
+// 128-token blocks: HW = 2 or 1 q heads per workgroup, four waves per head
+// ---------------------------------------------------------------------------
+// CoSA Appendix D.1 takes 128-row query tiles with one skip vote per tile, the row
+// groups first reducing their own rows and the partial results then combined.  Here
+// each of a head's four waves owns 32 rows of the 128-row block and writes its
+// partial margin to LDS; after the barrier every wave takes the max of the four.
+// A 128-token key block is two 64-key tiles in consecutive ring slots (tiles 2v and
+// 2v+1 of the window), so the ring schedule of the 64-token kernel applies with one
+// block per step: the key sides of both tiles (one running-max update and one vote
+// for the block), the barrier, then the value sides under one exponent base.
+// NPB: physical pages per logical block (128 / page_len); a 64-key tile spans SUB of
+// them, or lies in half of one 128-token page (NPB = 1, row offset 64 x).
+template <int HW, int NPB>
+__global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const PrefillArgs a, int heads_per_group,
+                                                                    int nsub) {
+  constexpr int B = 2 * kPage;  // tokens per logical block
+  constexpr int NW = 4 * HW;    // waves
+  constexpr int NT = 64 * NW;   // threads
+  constexpr int GW = NW / 2;    // waves that gather tiles (waves 0 .. GW-1: one per SIMD at HW = 2)
+  constexpr int SUB = NPB == 1 ? 1 : NPB / 2;  // physical pages per 64-key tile
+  constexpr int kWindow = window_len<NPB>();
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kPageBytes];
+  __shared__ WindowLds<NPB> wlds;
+  __shared__ uint8_t dec_lds[HW][kWindow];
+  __shared__ float mar_lds[HW][kWindow];
+  __shared__ float vote_val[HW][2][4];  // [head][step parity][quarter]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int quarter = wave & 3;  // rows 32*quarter .. +31 of the block
+  const int hl = wave >> 2;      // head within the workgroup
+  const int hi = lane >> 5;
+  const Unit u = decode_unit<HW, B>(a, heads_per_group, nsub, hl);
+  const bool skip_on = a.delta > 0.f;
+  const float scale_log2 = a.sm_scale * kLog2e;
+  const float tau2 = skip_threshold2(a, u.L);
+  const bool logging = a.decisions != nullptr;
+  LDS_PTR(uint8_t) ring_lds = (LDS_PTR(uint8_t))ring;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring_lds;
+
+  const int r_blk = quarter * 32 + (lane & 31);
+  const int c_tok = u.i * B + r_blk;
+  const bool row_ok = c_tok < u.L;
+  bf16x8_t qf[8];
+  load_q<B>(a, u, r_blk, row_ok, hi, qf);
+
+  // online-softmax state as in the 64-token kernel (m2 running max, b2 lazy base)
+  float m2 = -INFINITY, b2 = -INFINITY, l2 = 0.f;
+  f32x16_t o[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[nt][e] = 0.f;
+
+  for (int x = threadIdx.x; x < (u.n_pages + 31) / 32; x += NT) wlds.seen_bits[x] = 0u;
+
+  const int32_t* mrow = a.order_mask + ((int64_t)u.qb * a.hkv + u.g) * a.max_mask_len;
+  const uint16_t* kbase = a.k + (int64_t)u.g * a.kv_sh;
+  const uint16_t* vbase = a.v + (int64_t)u.g * a.kv_sh;
+  const bool gatherer = wave < GW;
+  TileGather<GW> tg;
+  tg.init(a.kv_st, gatherer ? wave : 0, lane);
+
+  for (int k0 = 0; k0 < u.len; k0 += kWindow) {
+    const int wl = min(kWindow, u.len - k0);
+    if (logging && quarter == 0)
+      for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
+    const int nv = resolve_window<NT, NPB, B>(a, u, mrow, k0, wl, wlds, wave, lane);
+    const int ntiles = 2 * nv;
+    auto k_slot = [&](int t) { return ring_addr + (uint32_t)(t % kRing) * kTileBytes; };
+    auto v_slot = [&](int t) { return ring_addr + (uint32_t)(kRing * kTileBytes) + (uint32_t)(t % kRing) * kTileBytes; };
+    // this wave's share of tile t (half t % 2 of visit t / 2); a second half wholly past
+    // the sequence end is read from the first half's rows (finite values, masked logits)
+    auto gather_tile = [&](int t, bool is_v) {
+      if (!gatherer || t >= ntiles) return;
+      const int blk = t >> 1;
+      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[blk]);
+      const int valid = u.L - (jp * B + (t & 1) * kPage);
+      const int xs = valid > 0 ? (t & 1) : 0;
+      const uint16_t* sub_base[SUB];
+#pragma unroll
+      for (int x = 0; x < SUB; ++x) {
+        const int ph = __builtin_amdgcn_readfirstlane(wlds.vis_phys[blk * NPB + (NPB == 1 ? 0 : xs * SUB + x)]);
+        sub_base[x] = (is_v ? vbase : kbase) + (int64_t)ph * a.kv_sp +
+                      (NPB == 1 ? (int64_t)(xs * kPage) * a.kv_st : (int64_t)0);
+      }
+      tg.template issue<SUB>(sub_base, a.page_len, is_v ? v_slot(t) : k_slot(t), valid, is_v, wave, lane);
+    };
+
+    // prologue: K tiles of block 0 resident; V of block 0 and K of block 1 in flight
+    gather_tile(0, false);
+    gather_tile(1, false);
+    if (nv > 0) {
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+    gather_tile(0, true);
+    gather_tile(1, true);
+    gather_tile(2, false);
+    gather_tile(3, false);
+
+    const bool vote = skip_on || logging;
+    for (int v = 0; v < nv; ++v) {
+      const int par = v & 1;
+      const int j = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      const int key0 = j * B;
+      // ---- key side (Eq. (1), (2), (5)) over the block's 128 keys
+      f32x16_t acc_a[2], acc_b[2];
+      qk_tile(k_slot(2 * v), qf, lane, acc_a);
+      qk_tile(k_slot(2 * v + 1), qf, lane, acc_b);
+      const bool diag = j == u.i;
+      mask_tile_at(acc_a, key0, c_tok, u.L, hi, diag || u.L - key0 < kPage);
+      mask_tile_at(acc_b, key0 + kPage, c_tok, u.L, hi, diag || u.L - key0 < B);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(acc_a[tt][e], acc_b[tt][e]));
+      const float mloc = permlane32_max(mx) * scale_log2;
+      const float mnew = fmaxf(m2, mloc);
+      const float dd = (row_ok && mloc != -INFINITY) ? (mloc - mnew) : -INFINITY;
+      const float marg = max_lanes32(dd);
+      if (vote && lane == 0) vote_val[hl][par][quarter] = marg;
+      // every gather issued since the last barrier (K of block v+1, V of block v) has
+      // landed for this wave
+      wait_vmcnt<0>();
+      // past the barrier: the K tiles of block v and the V tiles of block v-1 are free,
+      // block v+1's K and block v's V are resident, and the four partial margins are
+      // visible
+      lds_barrier();
+      float margin2 = -INFINITY;
+      if (vote) {
+        const float m01 = fmaxf(vote_val[hl][par][0], vote_val[hl][par][1]);
+        const float m23 = fmaxf(vote_val[hl][par][2], vote_val[hl][par][3]);
+        margin2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(m01, m23))));
+      }
+      gather_tile(2 * v + 4, false);
+      gather_tile(2 * v + 5, false);
+      gather_tile(2 * v + 2, true);
+      gather_tile(2 * v + 3, true);
+      // ---- value side of the block: both tiles under one exponent base
+      const bool skip = skip_on && (margin2 < tau2);
+      if (logging && quarter == 0 && lane == 0) {
+        dec_lds[hl][wlds.vis_k[v] - k0] = skip ? 1 : 0;
+        mar_lds[hl][wlds.vis_k[v] - k0] = margin2 * kLn2;
+      }
+      m2 = mnew;
+      if (!skip) {
+        maybe_rebase(m2, b2, l2, o);
+        bf16x8_t pb[4];
+        float rs = probs_tile(acc_a, scale_log2, b2, pb);
+        pv_tile(v_slot(2 * v), pb, lane, o);
+        rs += probs_tile(acc_b, scale_log2, b2, pb);
+        pv_tile(v_slot(2 * v + 1), pb, lane, o);
+        l2 += permlane32_sum(rs);
+      }
+    }
+    wait_vmcnt<0>();  // no tile gather may still be writing LDS past this point
+    __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
+    if (logging && quarter == 0) flush_log(a, u, k0, wl, dec_lds[hl], mar_lds[hl], lane);
+    __syncthreads();
+  }
+  if (logging && quarter == 0) fill_log_tail(a, u, lane);
+  store_output<B>(a, u, o, l2, b2, r_blk, row_ok, lane);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -782,6 +958,26 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                      a.max_mask_len, a.sched, a.error_count);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.block == 2 * kPage) {
+    // 128-token blocks: two heads (eight waves) per workgroup when the group size is even
+    const int hw = (G % 2 == 0) ? 2 : 1;
+    const int ns = G / hw;
+    const dim3 grid((unsigned)a.total_qblocks * (unsigned)a.hkv * (unsigned)ns);
+    const int npb = 2 * kPage / a.page_len;
+    auto launch = [&](auto hw_c, auto npb_c) {
+      constexpr int H = decltype(hw_c)::value, N = decltype(npb_c)::value;
+      hipLaunchKernelGGL((osk_prefill_b128_kernel<H, N>), grid, dim3(256 * H), 0, stream, a, G, ns);
+    };
+    auto by_npb = [&](auto hw_c) {
+      if (npb == 1) launch(hw_c, std::integral_constant<int, 1>{});
+      else if (npb == 2) launch(hw_c, std::integral_constant<int, 2>{});
+      else if (npb == 4) launch(hw_c, std::integral_constant<int, 4>{});
+      else launch(hw_c, std::integral_constant<int, 8>{});
+    };
+    if (hw == 2) by_npb(std::integral_constant<int, 2>{});
+    else by_npb(std::integral_constant<int, 1>{});
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)a.total_qblocks * (unsigned)a.hkv * (unsigned)nsub);
   const int sub = kPage / a.page_len;
   auto launch = [&](auto hw_c, auto sub_c) {

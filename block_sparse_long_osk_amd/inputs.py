@@ -11,8 +11,10 @@ Conventions
 * Values are drawn in fp32 and rounded to bfloat16 with round-to-nearest-even;
   the bfloat16 bit patterns (``uint16``) are the canonical inputs.
 * Layouts: Q is ``[T, Hq, d]`` (sequences packed along T); the K and V pools are
-  ``[n_phys, Hkv, P, d]`` pages of P = 64 tokens; page tables are
-  ``[num_seqs, max_pages]`` int32 padded with -1.
+  ``[n_phys, Hkv, P, d]`` pages of P = 64 tokens (or the workload's page size:
+  the same tokens re-paged); page tables are ``[num_seqs, max_pages]`` int32
+  padded with -1.  ``cu_qblocks`` counts the workload's logical blocks (64 or
+  128 tokens).
 
 Workloads (the five shapes the method is measured on)
 ----------------------------------------------------
@@ -78,8 +80,9 @@ class Workload:
     pool_seed: Optional[int] = None
     pool_pages: Optional[int] = None
     skipping: bool = True     # False: skip scale fixed at -1 (disabled)
-    page_size: int = 64       # tokens per physical KV page (16 or 32: the same tokens re-paged)
+    page_size: int = 64       # tokens per physical KV page (16, 32 or 128: the same tokens re-paged)
     tokens_of: Optional[str] = None  # workload whose tokens these are (re-paged): its skip scale applies
+    block_size: int = 64      # tokens per logical block (query block, mask id, vote): 64 or 128
 
     @property
     def total_tokens(self) -> int:
@@ -111,6 +114,12 @@ WORKLOADS["cfg4_128k_structured_p16"] = dataclasses.replace(
     WORKLOADS["cfg4_128k_structured"], name="cfg4_128k_structured_p16",
     description="cfg4_128k_structured with its KV cache in shuffled 16-token physical pages",
     page_size=16, pool_seed=1008, tokens_of="cfg4_128k_structured")
+# The 128K workload under 128-token logical blocks (one skip vote per 128-row query
+# block) over its 64-token physical pages: two pages per block.
+WORKLOADS["cfg4_128k_structured_b128"] = dataclasses.replace(
+    WORKLOADS["cfg4_128k_structured"], name="cfg4_128k_structured_b128",
+    description="cfg4_128k_structured with 128-token logical blocks over 64-token pages",
+    block_size=128, tokens_of="cfg4_128k_structured")
 WORKLOAD_ORDER = ["cfg1_2k_mha", "cfg2_16k_gqa", "cfg3_32k_structured",
                   "cfg4_128k_structured", "cfg5_paged_2seq"]
 
@@ -155,9 +164,13 @@ class Batch:
         return int(self.page_table.shape[1])
 
     @property
+    def block_size(self) -> int:
+        return int(self.workload.block_size)
+
+    @property
     def max_blocks(self) -> int:
-        """Logical 64-token blocks a page-table row addresses."""
-        return -(-self.max_pages * int(self.k_pool.shape[2]) // PAGE)
+        """Logical blocks a page-table row addresses."""
+        return -(-self.max_pages * int(self.k_pool.shape[2]) // self.block_size)
 
 
 def _unit_rows(rng: np.random.Generator, n: int, d: int) -> np.ndarray:
@@ -265,6 +278,10 @@ def generate(wl: Workload) -> Batch:
         if rem:
             k_bits[ph[n_full], :, :rem, :] = kb[n_full * PAGE:].transpose(1, 0, 2)
             v_bits[ph[n_full], :, :rem, :] = vb[n_full * PAGE:].transpose(1, 0, 2)
+    if wl.block_size != PAGE:
+        if wl.block_size % wl.page_size != 0:
+            raise ValueError("the page size must divide the block size")
+        cu_qblocks = np.concatenate([[0], np.cumsum(-(-lens // wl.block_size))]).astype(np.int32)
     bt = Batch(wl, q_bits, k_bits, v_bits, page_table, cu_seqlens, cu_qblocks, salient_all)
     if wl.page_size != PAGE:
         bt = repage(bt, wl.page_size, wl.pool_seed if wl.pool_seed is not None else 0)
@@ -272,30 +289,38 @@ def generate(wl: Workload) -> Batch:
 
 
 def repage(batch: Batch, page_size: int, seed: int) -> Batch:
-    """The same token rows stored in a pool of page_size-token physical pages (16 or 32;
-    a storage layout change only): the page-sized token ranges of every sequence go to
-    physical pages in the order of a permutation drawn from (seed, stream 4), with 3
-    spare pages; page-table rows are -1 padded."""
-    if PAGE % page_size != 0 or page_size == PAGE:
-        raise ValueError("page_size must be 16 or 32")
-    sub = PAGE // page_size
+    """The same token rows stored in a pool of page_size-token physical pages (16, 32 or
+    128, from a pool of 64-token pages; a storage layout change only): the page-sized
+    token ranges of every sequence go to physical pages in the order of a permutation
+    drawn from (seed, stream 4), with 3 spare pages; page-table rows are -1 padded;
+    rows of a page past its sequence's end are zero."""
+    if batch.k_pool.shape[2] != PAGE or page_size not in (16, 32, 128):
+        raise ValueError("re-pages a pool of 64-token pages into 16, 32 or 128-token pages")
     S = batch.num_seqs
     lens = np.diff(batch.cu_seqlens.astype(np.int64))
-    n_small = [int(-(-L // page_size)) for L in lens]
-    total = sum(n_small)
+    n_new = [int(-(-L // page_size)) for L in lens]
+    total = sum(n_new)
     perm = np.random.default_rng([seed, STREAM_POOL]).permutation(total + 3)
     hkv, d = batch.k_pool.shape[1], batch.k_pool.shape[3]
     k_new = np.zeros((total + 3, hkv, page_size, d), dtype=batch.k_pool.dtype)
     v_new = np.zeros_like(k_new)
-    pt = np.full((S, batch.page_table.shape[1] * sub), -1, dtype=np.int32)
+    width = -(-batch.page_table.shape[1] * PAGE // page_size)
+    pt = np.full((S, width), -1, dtype=np.int32)
     pos = 0
     for s in range(S):
-        for p in range(n_small[s]):
-            src = batch.page_table[s, p // sub]
-            r0 = (p % sub) * page_size
+        L = int(lens[s])
+        for p in range(n_new[s]):
             dst = perm[pos]
-            k_new[dst] = batch.k_pool[src, :, r0:r0 + page_size]
-            v_new[dst] = batch.v_pool[src, :, r0:r0 + page_size]
+            # token rows p*page_size .. min(L, (p+1)*page_size), taken 64-token page by page
+            t = p * page_size
+            t_end = min(L, (p + 1) * page_size)
+            while t < t_end:
+                src = batch.page_table[s, t // PAGE]
+                r = t % PAGE
+                n = min(PAGE - r, t_end - t)
+                k_new[dst, :, t - p * page_size:t - p * page_size + n] = batch.k_pool[src, :, r:r + n]
+                v_new[dst, :, t - p * page_size:t - p * page_size + n] = batch.v_pool[src, :, r:r + n]
+                t += n
             pt[s, p] = dst
             pos += 1
     return dataclasses.replace(batch, k_pool=k_new, v_pool=v_new, page_table=pt)

@@ -22,6 +22,7 @@ class DeviceBatch:
     cu_qblocks: "torch.Tensor"   # int32 [S+1]
     total_qblocks: int
     seq_lens: tuple
+    block_size: int = 64         # tokens per logical block (64 or 128)
 
     @property
     def num_kv_heads(self) -> int:
@@ -33,12 +34,12 @@ class DeviceBatch:
 
     @property
     def max_blocks(self) -> int:
-        """Logical 64-token blocks a page-table row addresses (mask ids, score rows)."""
-        return -(-self.page_table.shape[1] * self.k_pool.shape[2] // 64)
+        """Logical blocks a page-table row addresses (mask ids, score rows)."""
+        return -(-self.page_table.shape[1] * self.k_pool.shape[2] // self.block_size)
 
     def dims(self, max_mask_len: int, sm_scale: float = 0.0) -> binding.CosaOskDims:
         return binding.make_dims(self.q, self.k_pool, self.page_table, self.total_qblocks, max_mask_len,
-                                 sm_scale=sm_scale)
+                                 sm_scale=sm_scale, block_size=self.block_size)
 
 
 def _bits_to_bf16(t_np, device):
@@ -53,7 +54,8 @@ def upload(batch, device: str = "cuda") -> DeviceBatch:
     return DeviceBatch(q=_bits_to_bf16(batch.q, device), k_pool=_bits_to_bf16(batch.k_pool, device),
                        v_pool=_bits_to_bf16(batch.v_pool, device), page_table=i32(batch.page_table),
                        cu_seqlens=i32(batch.cu_seqlens), cu_qblocks=i32(batch.cu_qblocks),
-                       total_qblocks=int(batch.cu_qblocks[-1]), seq_lens=tuple(batch.workload.seq_lens))
+                       total_qblocks=int(batch.cu_qblocks[-1]), seq_lens=tuple(batch.workload.seq_lens),
+                       block_size=int(batch.block_size))
 
 
 def upload_mask(order_mask: np.ndarray, mask_len: np.ndarray, device: str = "cuda"):
@@ -157,10 +159,10 @@ def validate_mask(db: DeviceBatch, order_mask, mask_len, stream=None) -> np.ndar
 
 
 def dense_mask(db: DeviceBatch):
-    """Every causal page 0..i in ascending order (the dense baseline's mask), built on the host."""
+    """Every causal block 0..i in ascending order (the dense baseline's mask), built on the host."""
     rows = []
     for L in db.seq_lens:
-        rows += list(range(-(-L // 64)))
+        rows += list(range(-(-L // db.block_size)))
     width = max(rows) + 1
     om = np.full((db.total_qblocks, db.num_kv_heads, width), -1, dtype=np.int32)
     ml = np.zeros((db.total_qblocks, db.num_kv_heads), dtype=np.int32)

@@ -7,7 +7,7 @@
  * Block-sparse causal prefill attention over a paged KV cache, as the CoSA
  * paper ("Accelerating Long-Context Inference via Proxy-Kernel Co-Designed
  * Sparse Attention") defines its Ordered-Skipping Kernel (OSK): section 4.3 and
- * Appendix C, Algorithm A (attention loop).  Every 64-token query block i of a
+ * Appendix C, Algorithm A (attention loop).  Every query block i of a
  * sequence visits the logical KV pages listed in its computation-order mask
  * (section 4.2, Eq. (14): kept ids in visit order, -1 padding), in mask order,
  * through the sequence's page table (physical page jumping and any-order page
@@ -32,17 +32,18 @@
  * - Blocks and pages (CoSA Appendix D.1: the logical block size b and the
  *   physical KV-cache page size b_p are set independently; a logical block is
  *   resolved through one or more physical pages).  The logical block -- the query
- *   block, the mask's key block, the unit of a skip vote -- is b = 64 tokens.  The
- *   KV cache's physical pages hold b_p = page_size = 16, 32 or 64 tokens: logical
- *   block j of a sequence is its tokens 64 j .. 64 j + 63, token t stored in
- *   physical page page_table[s][t / b_p] at row t % b_p.  A logical block is used
- *   only if every physical page holding one of its tokens t < L is a valid page id
- *   (0 <= id < num_phys_pages); otherwise it is not visited, like an invalid id.
- *   max_blocks = ceil(max_pages_per_seq * page_size / 64) logical blocks per
- *   sequence are addressable; mask ids, the mask-width helpers and the builders'
- *   score rows count logical blocks.
- * - Supported: head_dim = 128, page_size 16, 32 or 64, bfloat16 Q/K/V/out,
- *   num_q_heads % num_kv_heads == 0.
+ *   block, the mask's key block, the unit of a skip vote -- is b = block_size = 64
+ *   or 128 tokens (Appendix D.1 uses 128: one vote per 128-row query tile).  The KV
+ *   cache's physical pages hold b_p = page_size = 16, 32 or 64 tokens, or 128 when
+ *   b = 128: logical block j of a sequence is its tokens b j .. b j + b - 1, token
+ *   t stored in physical page page_table[s][t / b_p] at row t % b_p.  A logical
+ *   block is used only if every physical page holding one of its tokens t < L is a
+ *   valid page id (0 <= id < num_phys_pages); otherwise it is not visited, like an
+ *   invalid id.  max_blocks = ceil(max_pages_per_seq * page_size / b) logical
+ *   blocks per sequence are addressable; mask ids, the mask-width helpers and the
+ *   builders' score rows count logical blocks.
+ * - Supported: head_dim = 128, block_size 64 or 128, page_size dividing it (16,
+ *   32, 64, 128), bfloat16 Q/K/V/out, num_q_heads % num_kv_heads == 0.
  *   Limits: total_qblocks <= 16384, max_mask_len <= 8191,
  *   max_blocks <= 16384 (<= 8192 for the mask builders),
  *   kv_stride_tok <= 2^24 elements (a page's byte offsets fit in 32 bits).
@@ -53,7 +54,7 @@
  *     k_pool,v_pool [num_phys_pages, num_kv_heads, page_size, 128] (same strides)
  *     page_table    int32 [num_seqs, max_pages_per_seq]   page-sized token range -> physical page
  *     cu_seqlens    int32 [num_seqs + 1]  token offsets; L_s = difference
- *     cu_qblocks    int32 [num_seqs + 1]  prefix sums of ceil(L_s / 64)
+ *     cu_qblocks    int32 [num_seqs + 1]  prefix sums of ceil(L_s / b)
  *     order_mask    int32 [total_qblocks, num_kv_heads, max_mask_len]
  *     mask_len      int32 [total_qblocks, num_kv_heads]
  *   A query block's global index is qb = cu_qblocks[s] + i.  The q heads of a KV
@@ -71,7 +72,7 @@
 extern "C" {
 #endif
 
-#define COSA_ABI_VERSION 1
+#define COSA_ABI_VERSION 2
 
 typedef enum {
   COSA_OK = 0,
@@ -96,14 +97,14 @@ typedef struct cosa_osk_dims {
   int32_t num_q_heads;        /* Hq */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;           /* must be 128 */
-  int32_t page_size;          /* tokens per physical KV page: 16, 32 or 64 */
+  int32_t page_size;          /* tokens per physical KV page: 16, 32, 64 (128 if block_size is 128) */
   int32_t total_q_tokens;     /* T = cu_seqlens[num_seqs] */
   int32_t total_qblocks;      /* cu_qblocks[num_seqs] */
   int32_t max_pages_per_seq;  /* row stride of page_table (physical pages per sequence) */
   int32_t num_phys_pages;     /* pool size; a physical id outside [0, n) is not visited */
   int32_t max_mask_len;       /* row stride of order_mask and of the decision log */
   float sm_scale;             /* logit scale; <= 0 selects 1/sqrt(head_dim) */
-  int32_t reserved;           /* must be 0 */
+  int32_t block_size;         /* tokens per logical block b: 64 (0 selects 64) or 128 */
   int64_t q_stride_tok, q_stride_head;                  /* elements */
   int64_t o_stride_tok, o_stride_head;                  /* elements */
   int64_t kv_stride_page, kv_stride_head, kv_stride_tok; /* elements, K and V alike */
@@ -132,7 +133,7 @@ cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_
  *   page_table, cu_seqlens, cu_qblocks, order_mask, mask_len  int32; read only.
  *       order_mask rows hold logical page ids in visit order; entries at
  *       positions >= mask_len are ignored; inside the row, ids < 0, ids >=
- *       ceil(L_s/64), ids > i and repeats of an earlier id are not visited
+ *       ceil(L_s/b), ids > i and repeats of an earlier id are not visited
  *       (cosa_validate_order_mask reports them).
  *   budget2   the skip scale Delta of Eq. (5).  Delta <= 0 disables in-kernel
  *             skipping (Delta = -1 is the pages' "off" value).  Otherwise the
@@ -238,7 +239,8 @@ size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims);
  * are written; dims->max_mask_len must be >= cosa_kap_mask_width(...).
  * kap_scores (nullable) fp32 and hrm_flags (nullable) uint8, both
  * [total_qblocks, Hkv, max_blocks]: s_ij and h_ij for j <= i, NaN / 0 after.
- * Supported: stride 8 or 16, and G * 64 / stride a power of two <= 32 (G = Hq / Hkv);
+ * Supported: b / stride = 4 or 8 samples per block (strides 16 or 8 at b = 64, 32 or
+ * 16 at b = 128), and G * b / stride a power of two <= 32 (G = Hq / Hkv);
  * max_blocks <= 8192; otherwise COSA_ERR_UNSUPPORTED.  The page-table entries
  * of a sequence's pages must be valid physical pages.  k_pool uses the dims' KV
  * strides.  Asynchronous on `stream`; the workspace is overwritten.
@@ -253,7 +255,7 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
  * Count malformed mask entries (PageWeaver notes section 2.1 conventions: such
  * entries add no interaction; the prefill treats them as not visited).
  * bad_counts: device int32[5], zeroed by the call, then incremented:
- *   [0] ids outside [0, ceil(L_s/64)) at positions < mask_len (includes -1),
+ *   [0] ids outside [0, ceil(L_s/b)) at positions < mask_len (includes -1),
  *   [1] non-causal ids (j > i), [2] repeated ids in a row,
  *   [3] mask_len outside [0, max_mask_len],
  *   [4] referenced page-table entries outside [0, num_phys_pages).

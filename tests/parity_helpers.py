@@ -14,6 +14,7 @@ import math
 import numpy as np
 
 from block_sparse_long_osk_amd import inputs
+from oracle import paging
 from oracle.osk import NOT_VISITED, ReplayDecisions, block_thresholds, osk_reference
 
 MAX_ABS = 1e-2
@@ -26,6 +27,17 @@ LSE_ABS = 2e-3
 def host_arrays(batch):
     return (inputs.bf16_bits_to_f32(batch.q), inputs.bf16_bits_to_f32(batch.k_pool),
             inputs.bf16_bits_to_f32(batch.v_pool))
+
+
+def oracle_arrays(batch):
+    """(q, k, v, page_table, B): float arrays with the pools at the batch's logical block
+    size B (the oracle's view when physical pages are smaller or larger than B)."""
+    q, k, v = host_arrays(batch)
+    B, P = batch.block_size, k.shape[2]
+    pt = batch.page_table
+    if P != B:
+        k, v, pt = paging.logical_view(k, v, pt, batch.cu_seqlens, P, block=B)
+    return q, k, v, pt, B
 
 
 def gpu_to_host(outputs):
@@ -41,25 +53,25 @@ def unit_rows(batch, units):
     Hq, Hkv = batch.q.shape[1], batch.k_pool.shape[1]
     G = Hq // Hkv
     rows = np.zeros((batch.q.shape[0], Hq), dtype=bool)
-    cu_qb, cu = batch.cu_qblocks, batch.cu_seqlens
+    cu_qb, cu, B = batch.cu_qblocks, batch.cu_seqlens, batch.block_size
     for qb, g in units:
         s = int(np.searchsorted(cu_qb, qb, side="right") - 1)
         i = qb - cu_qb[s]
-        t0 = cu[s] + 64 * i
-        t1 = min(cu[s + 1], t0 + 64)
+        t0 = cu[s] + B * i
+        t1 = min(cu[s + 1], t0 + B)
         rows[t0:t1, g * G:(g + 1) * G] = True
     return rows
 
 
 def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_log=True):
     """Oracle replay vs the GPU result; returns a stats dict, asserts the bars."""
-    q, k, v = host_arrays(batch)
+    q, k, v, pt, B = oracle_arrays(batch)
     Hq, Hkv = q.shape[1], k.shape[1]
     if units is None:
         units = [(qb, g) for qb in range(batch.total_qblocks) for g in range(Hkv)]
-    taus = block_thresholds(batch.cu_seqlens, delta)
+    taus = block_thresholds(batch.cu_seqlens, delta, page_size=B)
     rep = ReplayDecisions(gpu["decisions"], taus) if "decisions" in gpu else None
-    ref = osk_reference(q, k, v, batch.page_table, batch.cu_seqlens, order_mask, mask_len, delta,
+    ref = osk_reference(q, k, v, pt, batch.cu_seqlens, order_mask, mask_len, delta, page_size=B,
                         units=units, decision_override=rep)
     stats = {"units": len(units)}
     rows = unit_rows(batch, units)
@@ -97,8 +109,8 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
     cu_qb = batch.cu_qblocks
     for qb, g in units[: 4096]:
         s = int(np.searchsorted(cu_qb, qb, side="right") - 1)
-        t0 = batch.cu_seqlens[s] + 64 * (qb - cu_qb[s])
-        t1 = min(batch.cu_seqlens[s + 1], t0 + 64)
+        t0 = batch.cu_seqlens[s] + B * (qb - cu_qb[s])
+        t1 = min(batch.cu_seqlens[s + 1], t0 + B)
         G = Hq // Hkv
         for h in range(g * G, (g + 1) * G):
             a, b = gpu["out"][t0:t1, h], ref["out"][t0:t1, h]
@@ -119,9 +131,12 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
 
 def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4):
     """A skip scale giving about `fraction` skipped visits on this batch, from the
-    oracle's own (decision-independent) margins."""
-    q, k, v = host_arrays(batch)
-    ref = osk_reference(q, k, v, batch.page_table, batch.cu_seqlens, order_mask, mask_len, -1.0,
+    oracle's own (decision-independent) margins.  The threshold is put in the middle of
+    a gap of at least 2e-3 between consecutive distinct margins (the split nearest the
+    fraction), so that no margin is a near-tie and every decision is held exactly;
+    without such a gap, at the plain quantile."""
+    q, k, v, pt, B = oracle_arrays(batch)
+    ref = osk_reference(q, k, v, pt, batch.cu_seqlens, order_mask, mask_len, -1.0, page_size=B,
                         compute_output=False)
     m = ref["margins"]
     lnL = np.zeros(m.shape[0])
@@ -129,6 +144,9 @@ def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4):
         lnL[batch.cu_qblocks[s]:batch.cu_qblocks[s + 1]] = math.log(batch.cu_seqlens[s + 1] - batch.cu_seqlens[s])
     x = np.sort((m + lnL[:, None, None])[np.isfinite(m)])
     kq = int(round(fraction * x.size))
+    splits = np.flatnonzero(np.diff(x) > 2e-3) + 1      # x[k-1] < x[k] - 2e-3
+    if splits.size:
+        kq = int(splits[np.argmin(np.abs(splits - fraction * x.size))])
     return float(math.exp(0.5 * (x[kq - 1] + x[kq])))
 
 

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
-    assert binding.cosa_abi_version() == 1
+    assert binding.cosa_abi_version() == 2
     assert binding.cosa_status_string(-3).startswith("workspace")
 
 
@@ -70,7 +70,7 @@ def test_calibration_library_exports_and_host_checks():
 def good_dims(**kw):
     d = dict(num_seqs=1, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=64, total_q_tokens=4096,
              total_qblocks=64, max_pages_per_seq=64, num_phys_pages=64, max_mask_len=20, sm_scale=0.0,
-             reserved=0, q_stride_tok=32 * 128, q_stride_head=128, o_stride_tok=32 * 128, o_stride_head=128,
+             block_size=0, q_stride_tok=32 * 128, q_stride_head=128, o_stride_tok=32 * 128, o_stride_head=128,
              kv_stride_page=8 * 64 * 128, kv_stride_head=64 * 128, kv_stride_tok=128)
     d.update(kw)
     return CosaOskDims(**d)
@@ -90,7 +90,13 @@ def test_check_args_status_codes():
         (dict(max_pages_per_seq=20000), UNSUPPORTED), (dict(num_kv_heads=0), INVALID),
         (dict(q_stride_head=100), INVALID), (dict(kv_stride_tok=0), INVALID),
         (dict(total_q_tokens=64 * 64 + 1), INVALID), (dict(total_qblocks=65, total_q_tokens=64), INVALID),
-        (dict(reserved=1), INVALID), (dict(sm_scale=float("nan")), INVALID),
+        (dict(block_size=1), UNSUPPORTED), (dict(block_size=256), UNSUPPORTED), (dict(block_size=64), OK),
+        # 128-token blocks: pages of 16 .. 128 tokens; blocks of up to 128 query tokens
+        (dict(block_size=128, total_qblocks=32), OK), (dict(block_size=128, page_size=128, total_qblocks=32), OK),
+        (dict(block_size=128, page_size=16, total_qblocks=32), OK),
+        (dict(block_size=128, total_qblocks=31), INVALID),
+        (dict(block_size=128, page_size=256, total_qblocks=32), UNSUPPORTED),
+        (dict(sm_scale=float("nan")), INVALID),
         (dict(kv_stride_tok=(1 << 24) + 8), UNSUPPORTED), (dict(kv_stride_tok=1 << 24), OK),
     ]
     for kw, want in cases:
@@ -171,3 +177,11 @@ def test_kap_builder_rejects_bad_arguments():
     assert call(mode=1, dd=good_dims(max_mask_len=63)) == INVALID  # Top-p rows can hold every candidate
     assert call(wsb=16) == WORKSPACE
     assert call(dd=good_dims(max_mask_len=64, max_pages_per_seq=9000)) == UNSUPPORTED
+    # 128-token blocks: strides 32 and 16 give 4 and 8 samples per block, 8 gives 16.  An
+    # accepted stride reaches the workspace check (too small here: nothing is launched)
+    d128 = good_dims(max_mask_len=64, block_size=128, total_qblocks=32)
+    assert call(dd=d128, stride=32, wsb=16) == WORKSPACE
+    assert call(dd=d128, stride=16, wsb=16) == WORKSPACE
+    assert call(dd=d128, stride=8, wsb=16) == UNSUPPORTED
+    assert call(dd=d128, stride=48, wsb=16) == UNSUPPORTED
+    assert call(stride=16, wsb=16) == WORKSPACE and call(stride=8, wsb=16) == WORKSPACE

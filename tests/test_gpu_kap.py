@@ -16,7 +16,7 @@ import pytest
 
 from block_sparse_long_osk_amd import inputs
 from oracle import kap
-from tests.parity_helpers import host_arrays
+from tests.parity_helpers import oracle_arrays
 
 pytestmark = pytest.mark.gpu
 
@@ -50,12 +50,13 @@ def check_kap(rt, name, batch, stride, mode, budget, blocks=None):
     torch.cuda.synchronize()
     om_g, ml_g = om_d.cpu().numpy(), ml_d.cpu().numpy()
     sc_g, fl_g = sc_d.cpu().numpy(), fl_d.cpu().numpy()
-    q, k, _ = host_arrays(batch)
+    q, k, _, pt, B = oracle_arrays(batch)
     nqb = om_g.shape[0]
     want = list(range(nqb)) if blocks is None else list(blocks)
-    om_o, ml_o, sc_o, fl_o, hm_o = kap.build_kap_mask(q, k, batch.page_table, batch.cu_seqlens, Hkv, stride, mode,
-                                                      budget, width=om_g.shape[2], blocks=want, return_hmax=True)
-    starts = np.cumsum([0] + [-(-int(L) // 64) for L in np.diff(batch.cu_seqlens)])
+    om_o, ml_o, sc_o, fl_o, hm_o = kap.build_kap_mask(q, k, pt, batch.cu_seqlens, Hkv, stride, mode, budget,
+                                                      page_size=B, width=om_g.shape[2], blocks=want,
+                                                      return_hmax=True)
+    starts = np.cumsum([0] + [-(-int(L) // B) for L in np.diff(batch.cu_seqlens)])
     stats = dict(units=0, flag_ties=0, len_ties=0, max_score_err=0.0)
     for pos, qb in enumerate(want):
         sidx = int(np.searchsorted(starts, qb, side="right") - 1)

@@ -47,18 +47,33 @@ def test_structured_planting_is_visible_in_logits():
     assert min(page_mean[j] for j in sal) > max(page_mean[j] for j in others)
 
 
-@pytest.mark.parametrize("bp", [16, 32])
+@pytest.mark.parametrize("bp", [16, 32, 128])
 def test_repage_is_a_storage_change_only(bp):
     from oracle import paging
     wl = inputs.small_workload("rp", [64 * 6 + 17, 64 * 2, 5], 4, 2, generator="structured", seed=3, pool="shuffled")
     bt = inputs.generate(wl)
     rp = inputs.repage(bt, bp, 11)
-    assert rp.k_pool.shape[2] == bp and rp.max_blocks == bt.max_blocks
-    kl, vl, ptl = paging.logical_view(rp.k_pool, rp.v_pool, rp.page_table, rp.cu_seqlens, bp)
-    k0, v0, pt0 = paging.logical_view(bt.k_pool, bt.v_pool, bt.page_table, bt.cu_seqlens, 64)
+    assert rp.k_pool.shape[2] == bp
+    B = max(64, bp)   # the logical view at a block size both layouts divide
+    kl, vl, ptl = paging.logical_view(rp.k_pool, rp.v_pool, rp.page_table, rp.cu_seqlens, bp, block=B)
+    k0, v0, pt0 = paging.logical_view(bt.k_pool, bt.v_pool, bt.page_table, bt.cu_seqlens, 64, block=B)
     np.testing.assert_array_equal(ptl, pt0)
     np.testing.assert_array_equal(kl, k0)
     np.testing.assert_array_equal(vl, v0)
     # every physical page is used at most once
     used = rp.page_table[rp.page_table >= 0]
     assert used.size == np.unique(used).size
+
+
+def test_block128_workload_counts_128_token_blocks():
+    import dataclasses
+    wl = inputs.small_workload("b", [128 * 5 + 3, 64, 129], 4, 2, generator="iid", seed=2, pool="shuffled")
+    bt64 = inputs.generate(wl)
+    bt = inputs.generate(dataclasses.replace(wl, block_size=128))
+    assert list(bt.cu_qblocks) == [0, 6, 7, 9] and bt.block_size == 128
+    assert bt.max_blocks == -(-bt.max_pages * 64 // 128)
+    # the same tokens and pages as the 64-token workload
+    np.testing.assert_array_equal(bt.k_pool, bt64.k_pool)
+    np.testing.assert_array_equal(bt.page_table, bt64.page_table)
+    wl128 = inputs.WORKLOADS["cfg4_128k_structured_b128"]
+    assert wl128.block_size == 128 and wl128.page_size == 64 and wl128.seq_lens == (131072,)
