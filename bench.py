@@ -37,8 +37,12 @@ def block_flop(block_size: int) -> float:
     """One b x b x 128 contraction (QK^T or P V of one visited (q head, block))."""
     return TILE_FLOP * (block_size // 64) ** 2
 KAP_STRIDE = 16
-KERNEL_SOURCES = ["block_sparse_long_osk_amd/csrc/osk_prefill.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "osk_prefill_cfg4_128k_traffic.json")
+KERNEL_SOURCES = ["block_sparse_long_osk_amd/csrc/osk_prefill.hip", "block_sparse_long_osk_amd/csrc/osk_internal.h"]
+# FETCH_SIZE / WRITE_SIZE summaries per workload (used while the kernel sources are unchanged)
+TRAFFIC_FILES = {
+    "cfg4_128k_structured": os.path.join(ROOT, "profiles", "osk_prefill_cfg4_128k_traffic.json"),
+    "cfg4_128k_structured_b128": os.path.join(ROOT, "profiles", "osk_prefill_b128_cfg4_128k_traffic.json"),
+}
 
 
 def kernel_source_hash():
@@ -317,8 +321,9 @@ def main():
 
     # ---- roofline of the dominant kernel
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tfile = TRAFFIC_FILES.get(wl.name)
+    if tfile and os.path.exists(tfile):
+        with open(tfile) as f:
             tr = json.load(f)
         if tr.get("workload") == wl.name and tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
