@@ -22,8 +22,17 @@ What it computes (sources are the pages this project follows):
   CoSA section 3.3); the vote is taken over the block's valid rows (rows past L
   do not vote); a row that sees no key of a page does not veto.
 
+* Per-q-head page sets under grouped-query heads -- PageWeaver notes, section 2.2:
+  the heads of a KV group traverse the union U of their sets, and a membership
+  mask M[h, p] = 1[p in S_h] keeps each head's softmax to its own pages.  Here the
+  mask row of a KV head is the union in visit order and membership[qb, h, k] says
+  whether entry k belongs to q head h; a head takes part in a visit (key side,
+  running max, vote, value side) only at its own entries, so it sees exactly its
+  own pages in the union's order.
+
 Decision codes: 0 = computed, 1 = skipped in-kernel, 2 = not visited (mask
-padding, an id outside [0, n_pages), a non-causal id j > i, or a repeated id).
+padding, an id outside [0, n_pages), a non-causal id j > i, a repeated id, or an
+entry outside the head's membership).
 Margins are in natural-log units of the scaled logits; NaN where not visited.
 
 All arithmetic is float64 on the exact (bfloat16-valued) inputs.  The batched
@@ -152,7 +161,7 @@ def skip_threshold(delta: float, seq_len: int) -> Optional[float]:
 def osk_reference(q, k_pool, v_pool, page_table, cu_seqlens, order_mask, mask_len, delta: float,
                   page_size: int = 64, sm_scale: Optional[float] = None,
                   compute_output: bool = True, units: Optional[Sequence[tuple]] = None,
-                  decision_override=None, chunk_blocks: int = 128):
+                  decision_override=None, chunk_blocks: int = 128, membership=None):
     """Run the ordered online softmax with in-kernel skipping.
 
     q: [T, Hq, d]; k_pool, v_pool: [n_phys, Hkv, P, d]; page_table: [S, max_pages];
@@ -165,6 +174,8 @@ def osk_reference(q, k_pool, v_pool, page_table, cu_seqlens, order_mask, mask_le
     compute_output=False runs only the logits / running-max / vote pass (the
         decisions do not depend on the value side, since m is updated before the
         test whether or not the page is skipped).
+    membership: optional [total_qblocks, Hq, max_len] (nonzero = entry k of the KV
+        head's row belongs to q head h); None = every head takes every entry.
 
     Returns dict with out [T,Hq,d], lse [T,Hq], decisions [total_qblocks,Hq,max_len]
     (uint8), margins (float64, NaN where not visited); rows of units that were not
@@ -209,7 +220,8 @@ def osk_reference(q, k_pool, v_pool, page_table, cu_seqlens, order_mask, mask_le
         for c0 in range(0, len(blocks), chunk_blocks):
             blk = blocks[c0:c0 + chunk_blocks]
             res = _run_blocks(q, k_pool, v_pool, page_table[s], t0, L, n_pages, cu_qb[s], blk, g, heads,
-                              order_mask, mask_len, tau, sm_scale, P, compute_output, decision_override)
+                              order_mask, mask_len, tau, sm_scale, P, compute_output, decision_override,
+                              membership)
             qbs = cu_qb[s] + blk
             decisions[qbs[:, None], heads[None, :], :] = res["decisions"]
             margins[qbs[:, None], heads[None, :], :] = res["margins"]
@@ -225,7 +237,7 @@ def osk_reference(q, k_pool, v_pool, page_table, cu_seqlens, order_mask, mask_le
 
 
 def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, heads,
-                order_mask, mask_len, tau, sm_scale, P, compute_output, decision_override):
+                order_mask, mask_len, tau, sm_scale, P, compute_output, decision_override, membership=None):
     """All query blocks in `blocks` of one (sequence, KV head), stepped together
     through the visit index k.  State per (block, q head, row): m, l, o."""
     nb = len(blocks)
@@ -281,15 +293,20 @@ def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, h
             skip = np.zeros(margin.shape, dtype=bool)
         else:
             skip = margin < tau
+        # heads whose set holds this entry (all of them without a membership mask)
+        if membership is None:
+            mem = np.ones(margin.shape, dtype=bool)
+        else:
+            mem = np.asarray(membership[qbs[vb][:, None], heads[None, :], k]) != 0
         if decision_override is not None:
-            skip = decision_override(qbs[vb], heads, k, skip, margin)
-        decisions[vb, :, k] = np.where(skip, NOT_COMPUTED_SKIP, COMPUTED)
-        margins[vb, :, k] = margin
-        m[vb] = m_new
+            skip = decision_override(qbs[vb], heads, k, skip, margin, member=mem)
+        decisions[vb, :, k] = np.where(mem, np.where(skip, NOT_COMPUTED_SKIP, COMPUTED), NOT_VISITED)
+        margins[vb, :, k] = np.where(mem, margin, np.nan)
+        m[vb] = np.where(mem[..., None], m_new, m_old)
         if not compute_output:
             continue
         # lines 17-19 for the pages that are not skipped
-        comp = ~skip                                                     # [n, G]
+        comp = ~skip & mem                                               # [n, G]
         if not comp.any():
             continue
         alpha = np.where(np.isneginf(m_new), 1.0, np.exp(m_old - np.where(np.isneginf(m_new), 0.0, m_new)))
@@ -332,16 +349,18 @@ class ReplayDecisions:
         self.near_tie_flips = 0
         self.disagreements = []  # (qb, head, k, own, other, margin)
 
-    def __call__(self, qbs, heads, k, own_skip, margin):
+    def __call__(self, qbs, heads, k, own_skip, margin, member=None):
         oth = self.other[qbs[:, None], heads[None, :], k]                # [n, G]
         tau = self.taus[qbs][:, None]
-        near = np.isfinite(tau) & (np.abs(margin - tau) < NEAR_TIE)
+        if member is None:
+            member = np.ones(margin.shape, dtype=bool)
+        near = member & np.isfinite(tau) & (np.abs(margin - tau) < NEAR_TIE)
         self.near_ties += int(near.sum())
         oth_skip = oth == NOT_COMPUTED_SKIP
         valid_other = (oth == COMPUTED) | (oth == NOT_COMPUTED_SKIP)
         flip = near & valid_other & (oth_skip != own_skip)
         self.near_tie_flips += int(flip.sum())
-        bad = (~near) & ((~valid_other) | (oth_skip != own_skip))
+        bad = member & (~near) & ((~valid_other) | (oth_skip != own_skip))
         for a, b in zip(*np.nonzero(bad)):
             self.disagreements.append((int(qbs[a]), int(heads[b]), int(k), int(own_skip[a, b]),
                                        int(oth[a, b]), float(margin[a, b])))
