@@ -77,6 +77,16 @@ def lib():
                                           P, P, ctypes.c_size_t, P]
         L.cosa_validate_order_mask.restype = ctypes.c_int
         L.cosa_validate_order_mask.argtypes = [D, P, P, P, P, P, P, P]
+        L.cosa_osk_prefill_union.restype = ctypes.c_int
+        L.cosa_osk_prefill_union.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        L.cosa_union_mask_width.restype = ctypes.c_int32
+        L.cosa_union_mask_width.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_uint32]
+        L.cosa_build_union_mask_workspace_bytes.restype = ctypes.c_size_t
+        L.cosa_build_union_mask_workspace_bytes.argtypes = [D]
+        L.cosa_build_union_mask.restype = ctypes.c_int
+        L.cosa_build_union_mask.argtypes = [D, P, P, P, P, P, ctypes.c_float, ctypes.c_uint32, P, P, P, P, P,
+                                            ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -84,7 +94,8 @@ def lib():
 EXPORTED = ["cosa_abi_version", "cosa_status_string", "cosa_osk_workspace_bytes", "cosa_osk_check_args",
             "cosa_osk_prefill", "cosa_order_mask_width", "cosa_build_order_mask_workspace_bytes",
             "cosa_build_order_mask", "cosa_validate_order_mask", "cosa_kap_mask_width",
-            "cosa_build_kap_mask_workspace_bytes", "cosa_build_kap_mask"]
+            "cosa_build_kap_mask_workspace_bytes", "cosa_build_kap_mask", "cosa_osk_prefill_union",
+            "cosa_union_mask_width", "cosa_build_union_mask_workspace_bytes", "cosa_build_union_mask"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -204,3 +215,41 @@ def cosa_validate_order_mask(dims: CosaOskDims, page_table, cu_seqlens, cu_qbloc
     st = lib().cosa_validate_order_mask(ctypes.byref(dims), _ptr(page_table), _ptr(cu_seqlens), _ptr(cu_qblocks),
                                         _ptr(order_mask), _ptr(mask_len), _ptr(bad_counts), _stream(stream))
     _check(st, "cosa_validate_order_mask")
+
+
+def cosa_osk_prefill_union(dims: CosaOskDims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask,
+                           mask_len, membership, budget2: float, out, lse=None, decisions=None, margins=None,
+                           workspace=None, stream=None):
+    """The prefill with per-q-head membership of the union rows."""
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(cosa_osk_workspace_bytes(dims), 256), dtype=torch.uint8, device=q.device)
+    st = lib().cosa_osk_prefill_union(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                      _ptr(cu_seqlens), _ptr(cu_qblocks), _ptr(order_mask), _ptr(mask_len),
+                                      _ptr(membership), float(budget2), _ptr(out), _ptr(lse), _ptr(decisions),
+                                      _ptr(margins), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    _check(st, "cosa_osk_prefill_union")
+
+
+def cosa_union_mask_width(max_blocks_per_seq: int, group: int, budget1: float,
+                          flags: int = COSA_FORCE_FIRST | COSA_FORCE_DIAG) -> int:
+    return lib().cosa_union_mask_width(int(max_blocks_per_seq), int(group), float(budget1), int(flags))
+
+
+def cosa_build_union_mask_workspace_bytes(dims: CosaOskDims) -> int:
+    return lib().cosa_build_union_mask_workspace_bytes(ctypes.byref(dims))
+
+
+def cosa_build_union_mask(dims: CosaOskDims, q, k_pool, page_table, cu_seqlens, cu_qblocks, budget1: float,
+                          order_mask, mask_len, membership, head_len, flags: int = COSA_FORCE_FIRST | COSA_FORCE_DIAG,
+                          workspace=None, stream=None):
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(cosa_build_union_mask_workspace_bytes(dims), 256), dtype=torch.uint8,
+                                device=q.device)
+    st = lib().cosa_build_union_mask(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(page_table), _ptr(cu_seqlens),
+                                     _ptr(cu_qblocks), float(budget1), int(flags), _ptr(order_mask), _ptr(mask_len),
+                                     _ptr(membership), _ptr(head_len), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "cosa_build_union_mask")

@@ -102,11 +102,15 @@ cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_
   return COSA_OK;
 }
 
-cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const void* k_pool, const void* v_pool,
-                               const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
-                               const int32_t* order_mask, const int32_t* mask_len, float budget2, void* out,
-                               float* lse, uint8_t* decisions, float* margins, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// The prefill with an optional membership mask (null: every q head takes every entry).
+static cosa_status_t prefill_impl(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* page_table, const int32_t* cu_seqlens,
+                                  const int32_t* cu_qblocks, const int32_t* order_mask, const int32_t* mask_len,
+                                  const uint8_t* membership, float budget2, void* out, float* lse,
+                                  uint8_t* decisions, float* margins, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
   cosa_status_t st = cosa_osk_check_args(dims, workspace_bytes);
   if (st != COSA_OK) return st;
   if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr ||
@@ -117,7 +121,7 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   if (margins != nullptr && decisions == nullptr) return COSA_ERR_INVALID_ARG;
   if (isnan(budget2)) return COSA_ERR_INVALID_ARG;
   if (workspace == nullptr || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
-  cosa_osk::PrefillArgs a;
+  cosa_osk::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_pool);
   a.v = static_cast<const uint16_t*>(v_pool);
@@ -126,6 +130,7 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   a.cu_qblocks = cu_qblocks;
   a.order_mask = order_mask;
   a.mask_len = mask_len;
+  a.membership = membership;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.decisions = decisions;
@@ -152,6 +157,28 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
   a.sm_scale = resolved_scale(dims);
   a.delta = budget2;
   return cosa_osk::launch_prefill(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
+}
+
+extern "C" {
+
+cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                               const int32_t* order_mask, const int32_t* mask_len, float budget2, void* out,
+                               float* lse, uint8_t* decisions, float* margins, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return prefill_impl(dims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len, nullptr,
+                      budget2, out, lse, decisions, margins, workspace, workspace_bytes, stream);
+}
+
+cosa_status_t cosa_osk_prefill_union(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* page_table, const int32_t* cu_seqlens,
+                                     const int32_t* cu_qblocks, const int32_t* order_mask, const int32_t* mask_len,
+                                     const uint8_t* membership, float budget2, void* out, float* lse,
+                                     uint8_t* decisions, float* margins, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (membership == nullptr && dims != nullptr && dims->max_mask_len > 0) return COSA_ERR_INVALID_ARG;
+  return prefill_impl(dims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len,
+                      membership, budget2, out, lse, decisions, margins, workspace, workspace_bytes, stream);
 }
 
 int32_t cosa_order_mask_width(int32_t max_blocks_per_seq, float budget1, uint32_t flags) {
@@ -198,7 +225,7 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   if (dims->max_mask_len < cosa_order_mask_width(max_blocks(dims), budget1, flags)) return COSA_ERR_INVALID_ARG;
   const size_t need = cosa_build_order_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
-  cosa_osk::BuilderArgs a;
+  cosa_osk::BuilderArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_pool);
   a.page_table = page_table;
@@ -230,6 +257,90 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   a.budget1 = budget1;
   a.flags = flags;
   return cosa_osk::launch_build_order_mask(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
+}
+
+int32_t cosa_union_mask_width(int32_t max_blocks_per_seq, int32_t group, float budget1, uint32_t flags) {
+  if (max_blocks_per_seq < 1 || group < 1) return -1;
+  int64_t width = 0;
+  for (int32_t i = 0; i < max_blocks_per_seq; ++i) {
+    int nf = 0;
+    if (flags & COSA_FORCE_FIRST) ++nf;
+    if ((flags & COSA_FORCE_DIAG) && !((flags & COSA_FORCE_FIRST) && i == 0)) ++nf;
+    const int64_t len = std::min<int64_t>((int64_t)i + 1, (int64_t)group * (nf + keep_count(budget1, i + 1 - nf)));
+    if (len > width) width = len;
+  }
+  return (int32_t)width;
+}
+
+// union-builder workspace: the shared builder's regions, then each head's block means
+// [total_qblocks, Hq, 128] fp32 and score rows [total_qblocks, Hq, max_blocks] fp32
+static size_t union_head_pool_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * d->num_q_heads * kHeadDim * sizeof(float) + 1);
+}
+static size_t union_head_score_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * d->num_q_heads * (size_t)std::max(max_blocks(d), 0) * sizeof(float) +
+                  1);
+}
+
+size_t cosa_build_union_mask_workspace_bytes(const cosa_osk_dims_t* dims) {
+  if (dims == nullptr || dims->total_qblocks < 0 || dims->num_kv_heads < 1 || dims->num_q_heads < 1) return 0;
+  return cosa_build_order_mask_workspace_bytes(dims) + union_head_pool_bytes(dims) + union_head_score_bytes(dims);
+}
+
+cosa_status_t cosa_build_union_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                    const int32_t* page_table, const int32_t* cu_seqlens, const int32_t* cu_qblocks,
+                                    float budget1, uint32_t flags, int32_t* order_mask, int32_t* mask_len,
+                                    uint8_t* membership, int32_t* head_len, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  if (max_blocks(dims) > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
+  const int32_t G = dims->num_q_heads / dims->num_kv_heads;
+  if (G > 32) return COSA_ERR_UNSUPPORTED;  // a candidate's head bits are one 32-bit word
+  if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
+      order_mask == nullptr || mask_len == nullptr || membership == nullptr || head_len == nullptr)
+    return COSA_ERR_INVALID_ARG;
+  if (!(budget1 >= 0.f && budget1 <= 1.f)) return COSA_ERR_INVALID_ARG;
+  if ((flags & ~(uint32_t)(COSA_FORCE_FIRST | COSA_FORCE_DIAG)) != 0u) return COSA_ERR_INVALID_ARG;
+  if (dims->max_mask_len < cosa_union_mask_width(max_blocks(dims), G, budget1, flags)) return COSA_ERR_INVALID_ARG;
+  const size_t need = cosa_build_union_mask_workspace_bytes(dims);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  cosa_osk::BuilderArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_pool);
+  a.page_table = page_table;
+  a.cu_seqlens = cu_seqlens;
+  a.cu_qblocks = cu_qblocks;
+  a.order_mask = order_mask;
+  a.mask_len = mask_len;
+  a.scores = nullptr;
+  a.qbar = reinterpret_cast<float*>(ws);
+  a.kbar = reinterpret_cast<float*>(ws + builder_pool_bytes(dims));
+  a.score_rows = reinterpret_cast<float*>(ws + 2 * builder_pool_bytes(dims));
+  a.qbar_heads = reinterpret_cast<float*>(ws + cosa_build_order_mask_workspace_bytes(dims));
+  a.head_score_rows =
+      reinterpret_cast<float*>(ws + cosa_build_order_mask_workspace_bytes(dims) + union_head_pool_bytes(dims));
+  a.membership = membership;
+  a.head_len = head_len;
+  a.q_st = dims->q_stride_tok;
+  a.q_sh = dims->q_stride_head;
+  a.kv_sp = dims->kv_stride_page;
+  a.kv_sh = dims->kv_stride_head;
+  a.kv_st = dims->kv_stride_tok;
+  a.num_seqs = dims->num_seqs;
+  a.hq = dims->num_q_heads;
+  a.hkv = dims->num_kv_heads;
+  a.total_qblocks = dims->total_qblocks;
+  a.max_pages = max_blocks(dims);
+  a.pt_stride = dims->max_pages_per_seq;
+  a.page_len = dims->page_size;
+  a.block = block_of(dims);
+  a.num_phys = dims->num_phys_pages;
+  a.max_mask_len = dims->max_mask_len;
+  a.budget1 = budget1;
+  a.flags = flags;
+  return cosa_osk::launch_build_union_mask(a, stream) == hipSuccess ? COSA_OK : COSA_ERR_HIP;
 }
 
 int32_t cosa_kap_mask_width(int32_t max_blocks_per_seq, int32_t mode, float budget) {
@@ -280,7 +391,7 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   if (dims->max_mask_len < cosa_kap_mask_width(max_blocks(dims), mode, budget)) return COSA_ERR_INVALID_ARG;
   const size_t need = cosa_build_kap_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
-  cosa_osk::KapArgs a;
+  cosa_osk::KapArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k_pool);
   a.page_table = page_table;
@@ -324,7 +435,7 @@ cosa_status_t cosa_validate_order_mask(const cosa_osk_dims_t* dims, const int32_
   if (page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr || mask_len == nullptr ||
       bad_counts == nullptr || (order_mask == nullptr && dims->max_mask_len > 0))
     return COSA_ERR_INVALID_ARG;
-  cosa_osk::ValidateArgs a;
+  cosa_osk::ValidateArgs a{};
   a.page_table = page_table;
   a.cu_seqlens = cu_seqlens;
   a.cu_qblocks = cu_qblocks;

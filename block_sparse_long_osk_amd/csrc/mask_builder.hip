@@ -18,6 +18,17 @@
 //   select one workgroup per (query block, KV head): forced pages set aside, a
 //          bitonic sort of the rest by (score desc, id asc) in LDS, and a merge of
 //          the forced pages into the top n_keep by the same key.
+//
+// Per-q-head sets (PageWeaver notes, section 2.2: the heads of a group traverse the
+// union of their sets, a membership mask keeping each head to its own): each q head
+// selects its own set by the same rule from its own score qbar_h . kbar (qbar_h its
+// block mean); the KV head's row is the union, visited in the group-score order of
+// the shared mask, with membership[qb, h, k] = 1 iff entry k is in head h's set.
+//   pool_heads  one workgroup per (query block, KV head): the G per-head means;
+//   score       the score kernel above over per-head rows;
+//   union       one workgroup per (query block, KV head): G bitonic sorts of the
+//               heads' candidates by their own scores mark each head's top n_keep,
+//               then one sort of the union by the group score writes the row.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -95,15 +106,56 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
   }
 }
 
+// Each q head's block mean: thread t handles dims 8*(t%16) .. +8 of rows t/16, +16, ...
+__global__ __launch_bounds__(256) void mask_pool_heads_kernel(const BuilderArgs a) {
+  __shared__ float red[16][kHeadDim];
+  const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int chunk = tid & 15, rg = tid >> 4;
+  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
+  const int i = qb - a.cu_qblocks[s];
+  const int tok0 = a.cu_seqlens[s];
+  const int L = a.cu_seqlens[s + 1] - tok0;
+  const int rows = min(a.block, L - i * a.block);
+  const int G = a.hq / a.hkv;
+  for (int hh = 0; hh < G; ++hh) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t* qh = a.q + (int64_t)tok0 * a.q_st + (int64_t)(g * G + hh) * a.q_sh + chunk * 8;
+    for (int r = rg; r < rows; r += 16) {
+      const uint4 w = *(const uint4*)(qh + (int64_t)(i * a.block + r) * a.q_st);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(u[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg][chunk * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < kHeadDim) {
+      float t = 0.f;
+      for (int x = 0; x < 16; ++x) t += red[x][tid];
+      a.qbar_heads[((int64_t)qb * a.hq + g * G + hh) * kHeadDim + tid] = t / (float)rows;
+    }
+    __syncthreads();
+  }
+}
+
 // Query blocks per score workgroup: each pooled key row is read once for the group.
 constexpr int kScoreGroup = 8;
 
 // score_j = qbar . kbar_j (fp32, dims in order) for the causal pages j <= i of
-// kScoreGroup consecutive query blocks of one sequence and KV head; rows are
-// written for j <= i only.
+// kScoreGroup consecutive query blocks of one sequence and score row r; rows are
+// written for j <= i only.  HEADS = false: r = KV head g (the group's pooled query,
+// score_rows); HEADS = true: r = q head h of KV head h / G (qbar_heads, head_score_rows).
+template <bool HEADS>
 __global__ __launch_bounds__(256) void mask_score_kernel(const BuilderArgs a) {
   __shared__ float qs[kScoreGroup][kHeadDim];
-  const int gi = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int gi = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int nr = HEADS ? a.hq : a.hkv;                 // score rows per query block
+  const int g = HEADS ? r / (a.hq / a.hkv) : r;        // the KV head of row r
+  const float* qsrc = HEADS ? a.qbar_heads : a.qbar;
+  float* dst = HEADS ? a.head_score_rows : a.score_rows;
   // the sequence of group gi (groups do not straddle sequences)
   int s = 0, base = 0;
   for (; s < a.num_seqs; ++s) {
@@ -117,7 +169,7 @@ __global__ __launch_bounds__(256) void mask_score_kernel(const BuilderArgs a) {
   const int ng = min(kScoreGroup, a.cu_qblocks[s + 1] - qb0 - i0);
   for (int x = tid; x < kScoreGroup * kHeadDim; x += 256) {
     const int q = x / kHeadDim, d = x % kHeadDim;
-    qs[q][d] = q < ng ? a.qbar[((int64_t)(qb0 + i0 + q) * a.hkv + g) * kHeadDim + d] : 0.f;
+    qs[q][d] = q < ng ? qsrc[((int64_t)(qb0 + i0 + q) * nr + r) * kHeadDim + d] : 0.f;
   }
   __syncthreads();
   // block indices are clamped to the page-table width as in the select kernel
@@ -140,7 +192,7 @@ __global__ __launch_bounds__(256) void mask_score_kernel(const BuilderArgs a) {
 #pragma unroll
     for (int q = 0; q < kScoreGroup; ++q)
       if (q < ng && j <= min(i0 + q, a.max_pages - 1))
-        a.score_rows[((int64_t)(qb0 + i0 + q) * a.hkv + g) * a.max_pages + j] = acc[q];
+        dst[((int64_t)(qb0 + i0 + q) * nr + r) * a.max_pages + j] = acc[q];
   }
 }
 
@@ -231,13 +283,115 @@ hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   // groups of kScoreGroup blocks per sequence: at most total_qblocks / kScoreGroup + num_seqs
   const dim3 sgrid((unsigned)(a.total_qblocks / kScoreGroup + a.num_seqs), (unsigned)a.hkv);
-  hipLaunchKernelGGL(mask_score_kernel, sgrid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(mask_score_kernel<false>, sgrid, dim3(256), 0, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   // sort keys in LDS sized for the longest row (fewer workgroups per CU otherwise)
   int cap = 1;
   while (cap < a.max_pages) cap <<= 1;
   hipLaunchKernelGGL(mask_select_kernel, grid, dim3(256), (size_t)cap * sizeof(uint64_t), stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// union of per-q-head sets with membership
+// ---------------------------------------------------------------------------
+// ascending bitonic sort of n (a power of two) keys in LDS by the workgroup's 256 threads
+__device__ __forceinline__ void bitonic_lds(uint64_t* keys, int n, int tid) {
+  for (int kk = 2; kk <= n; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = tid; x < n; x += 256) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const uint64_t p = keys[x], q = keys[y];
+          const bool up = (x & kk) == 0;
+          if ((p > q) == up) { keys[x] = q; keys[y] = p; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// dynamic LDS: keys [cap] uint64, then the candidates' head bits [cap] uint32 (bit hh:
+// candidate j is in head g*G + hh's set); cap a power of two >= max_pages
+__global__ __launch_bounds__(256) void union_select_kernel(const BuilderArgs a, int cap) {
+  extern __shared__ uint64_t keys[];
+  uint32_t* bits = reinterpret_cast<uint32_t*>(keys + cap);
+  __shared__ int s_count;
+  const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int G = a.hq / a.hkv;
+  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
+  const int i = min(qb - a.cu_qblocks[s], a.max_pages - 1);
+  const bool f_first = (a.flags & 1u) != 0u;
+  const bool f_diag = (a.flags & 2u) != 0u && !(f_first && i == 0);
+  const int nf = (f_first ? 1 : 0) + (f_diag ? 1 : 0);
+  const int nrest = i + 1 - nf;
+  const int nkeep = keep_count(a.budget1, nrest);
+  const uint32_t all = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
+  auto forced = [&](int j) { return (f_first && j == 0) || (f_diag && j == i); };
+  for (int j = tid; j <= i; j += 256) bits[j] = forced(j) ? all : 0u;
+  if (tid == 0) s_count = 0;
+  int N = 1;
+  while (N < nrest) N <<= 1;
+  // each head's top nkeep of the non-forced candidates by its own score
+  for (int hh = 0; hh < G; ++hh) {
+    const float* srow = a.head_score_rows + ((int64_t)qb * a.hq + g * G + hh) * a.max_pages;
+    __syncthreads();  // the previous head's reads of keys are done
+    for (int j = tid; j <= i; j += 256)
+      if (!forced(j)) keys[j - ((f_first && j > 0) ? 1 : 0)] = sort_key(srow[j], j);
+    for (int x = nrest + tid; x < N; x += 256) keys[x] = ~0ull;
+    __syncthreads();
+    bitonic_lds(keys, N, tid);
+    for (int x = tid; x < nkeep; x += 256) bits[(int)(keys[x] & 0xffffffffu)] |= 1u << hh;
+  }
+  __syncthreads();
+  // the union, in the group score's order (score descending, id ascending)
+  int N2 = 1;
+  while (N2 < i + 1) N2 <<= 1;
+  const float* grow = a.score_rows + ((int64_t)qb * a.hkv + g) * a.max_pages;
+  int mine = 0;
+  for (int j = tid; j < N2; j += 256) {
+    const bool in = j <= i && bits[j] != 0u;
+    keys[j] = in ? sort_key(grow[j], j) : ~0ull;
+    mine += in ? 1 : 0;
+  }
+  if (mine) atomicAdd(&s_count, mine);
+  __syncthreads();
+  bitonic_lds(keys, N2, tid);
+  const int nu = min(s_count, a.max_mask_len);
+  int32_t* row = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
+  for (int x = tid; x < a.max_mask_len; x += 256) {
+    const int id = x < nu ? (int)(keys[x] & 0xffffffffu) : -1;
+    row[x] = id;
+    const uint32_t b = id >= 0 ? bits[id] : 0u;
+    for (int hh = 0; hh < G; ++hh)
+      a.membership[((int64_t)qb * a.hq + g * G + hh) * a.max_mask_len + x] = (uint8_t)((b >> hh) & 1u);
+  }
+  if (tid == 0) a.mask_len[(int64_t)qb * a.hkv + g] = nu;
+  if (tid < G) a.head_len[(int64_t)qb * a.hq + g * G + tid] = nf + nkeep;
+}
+
+hipError_t launch_build_union_mask(const BuilderArgs& a, hipStream_t stream) {
+  if (a.total_qblocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.total_qblocks, (unsigned)a.hkv);
+  hipLaunchKernelGGL(mask_pool_kernel, grid, dim3(256), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mask_pool_heads_kernel, grid, dim3(256), 0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const unsigned ngroups = (unsigned)(a.total_qblocks / kScoreGroup + a.num_seqs);
+  hipLaunchKernelGGL(mask_score_kernel<false>, dim3(ngroups, (unsigned)a.hkv), dim3(256), 0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mask_score_kernel<true>, dim3(ngroups, (unsigned)a.hq), dim3(256), 0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int cap = 1;
+  while (cap < a.max_pages) cap <<= 1;
+  hipLaunchKernelGGL(union_select_kernel, grid, dim3(256), (size_t)cap * (sizeof(uint64_t) + sizeof(uint32_t)),
+                     stream, a, cap);
   return hipGetLastError();
 }
 

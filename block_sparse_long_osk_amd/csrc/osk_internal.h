@@ -31,6 +31,7 @@ struct PrefillArgs {
   const int32_t* cu_qblocks;
   const int32_t* order_mask;
   const int32_t* mask_len;
+  const uint8_t* membership;  // nullable: [total_qblocks, hq, max_mask_len], entry k belongs to q head h
   uint16_t* out;
   float* lse;
   uint8_t* decisions;
@@ -57,6 +58,11 @@ struct BuilderArgs {
   float* qbar;        // workspace [total_qblocks, hkv, 128]
   float* kbar;        // workspace [total_qblocks, hkv, 128]
   float* score_rows;  // [total_qblocks, hkv, max_pages]: scores, or workspace when scores is null
+  // per-q-head sets (union builder only; null otherwise)
+  float* qbar_heads;       // workspace [total_qblocks, hq, 128]: each head's block mean
+  float* head_score_rows;  // workspace [total_qblocks, hq, max_pages]
+  uint8_t* membership;     // [total_qblocks, hq, max_mask_len]
+  int32_t* head_len;       // [total_qblocks, hq]
   int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
   int32_t pt_stride, page_len, block;
@@ -119,6 +125,7 @@ __device__ __forceinline__ bool block_phys(const int32_t* pt_row, int n_pt, int 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_build_kap_mask(const KapArgs& a, hipStream_t stream);
 hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream);
+hipError_t launch_build_union_mask(const BuilderArgs& a, hipStream_t stream);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 
 }  // namespace cosa_osk

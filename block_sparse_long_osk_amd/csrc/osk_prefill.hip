@@ -93,6 +93,12 @@ __device__ __forceinline__ float max_lanes32(float x) {
   const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
   return fmaxf(a, b);
 }
+// x * y rounded by itself: never fused into a later add or subtract, so that
+// m_loc - max(m, m_loc) is exactly 0 for a row whose running max moves to m_loc.
+__device__ __forceinline__ float mul_unfused(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -362,6 +368,8 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Unit& u, int 
 }
 
 // Visit list of one window of the mask row, in LDS (NPB physical page ids per block).
+// raw_id and vis_j hold the block id in bits 0..15 and, in bits 16 + hl, whether the
+// entry belongs to the workgroup's head hl (all set without a membership mask).
 template <int NPB>
 struct WindowLds {
   static constexpr int kWin = window_len<NPB>();
@@ -376,16 +384,25 @@ struct WindowLds {
 
 // Resolve mask entries k0 .. k0+wl-1 into the window's visit list: an entry is
 // visited when its id is a causal logical block of the sequence (0 <= id <= i, id
-// below the block count) whose physical pages are valid, and only at its first
-// occurrence in the row (bitmap over the sequence's blocks, kept across windows).
+// below the block count) whose physical pages are valid, only at its first
+// occurrence in the row (bitmap over the sequence's blocks, kept across windows),
+// and only if it belongs to one of the workgroup's HW heads h_first .. h_first+HW-1
+// (membership mask; a repeated id is not visited by any head).
 // B: tokens per logical block; NPB = B / page_len physical pages per block.
 // Returns the number of visits.  Called by every thread of the workgroup; ends with
 // a barrier.
-template <int NT, int NPB, int B>
+template <int NT, int NPB, int B, int HW>
 __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& u, const int32_t* mrow, int k0,
-                                              int wl, WindowLds<NPB>& w, int wave, int lane) {
+                                              int wl, WindowLds<NPB>& w, int wave, int lane, int h_first) {
   for (int e = threadIdx.x; e < wl; e += NT) {
     const int id = mrow[k0 + e];
+    int mbits = (1 << HW) - 1;
+    if (a.membership != nullptr) {
+      mbits = 0;
+      const uint8_t* mem = a.membership + ((int64_t)u.qb * a.hq + h_first) * a.max_mask_len + k0 + e;
+#pragma unroll
+      for (int x = 0; x < HW; ++x) mbits |= mem[(int64_t)x * a.max_mask_len] != 0 ? (1 << x) : 0;
+    }
     int ph[NPB];
     bool ok = false;
     if (id >= 0 && id < u.n_pages && id <= u.i) {
@@ -396,7 +413,7 @@ __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& 
         ok = block_phys(u.pt_row, a.pt_stride, id, u.L, a.page_len, B, a.num_phys, ph);
       }
     }
-    w.raw_id[e] = ok ? id : -1;
+    w.raw_id[e] = ok ? (id | (mbits << 16)) : -1;
 #pragma unroll
     for (int x = 0; x < NPB; ++x) w.raw_phys[e * NPB + x] = ok ? ph[x] : -1;
   }
@@ -406,7 +423,8 @@ __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& 
     int count = 0;
     for (int c0 = 0; c0 < wl; c0 += 64) {
       const int e = c0 + lane;
-      const int id = e < wl ? w.raw_id[e] : -1;
+      const int raw = e < wl ? w.raw_id[e] : -1;
+      const int id = raw >= 0 ? (raw & 0xFFFF) : -1;
       bool keep = id >= 0;
       const uint32_t bit = 1u << (id & 31);
       bool coll = false;
@@ -422,12 +440,15 @@ __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& 
         }
         keep = keep && !dup;
       }
-      const uint64_t km = __ballot(keep);
-      if (keep) {
+      // first occurrences are marked seen whether or not one of this workgroup's heads
+      // takes them; the workgroup visits those that belong to one of its heads
+      const bool visit = keep && (raw >> 16) != 0;
+      const uint64_t km = __ballot(visit);
+      if (visit) {
         const int p = count + __popcll(km & ((1ull << lane) - 1ull));
 #pragma unroll
         for (int x = 0; x < NPB; ++x) w.vis_phys[p * NPB + x] = w.raw_phys[e * NPB + x];
-        w.vis_j[p] = id;
+        w.vis_j[p] = raw;
         w.vis_k[p] = k0 + e;
       }
       count += __popcll(km);
@@ -495,7 +516,7 @@ __device__ __forceinline__ float rowmax2(const f32x16_t (&acc)[2], float scale_l
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[tt][e]);
-  return permlane32_max(mx) * scale_log2;
+  return mul_unfused(permlane32_max(mx), scale_log2);
 }
 __device__ __forceinline__ float mask_rowmax2(f32x16_t (&acc)[2], int j, int i, int r_blk, int L, int hi,
                                               float scale_log2) {
@@ -630,7 +651,9 @@ __device__ __forceinline__ float skip_threshold2(const PrefillArgs& a, int L) {
 // margins and its value side unless it is skipped.  Every page's arithmetic is
 // exactly that of visiting the pages one at a time.  Every wave runs the same
 // number of barriers (the visit count is workgroup-uniform), so no wait can hang.
-template <int HW, int SUB>
+// MEMB: a membership mask restricts each head to its own entries (otherwise every head
+// takes every visit and the membership tests fold away).
+template <int HW, int SUB, bool MEMB>
 __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const PrefillArgs a, int heads_per_group,
                                                                     int nsub) {
   constexpr int NW = 2 * HW;   // waves
@@ -684,7 +707,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     const int wl = min(kWindow, u.len - k0);
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
-    const int nv = resolve_window<NT, SUB, kPage>(a, u, mrow, k0, wl, wlds, wave, lane);
+    const int nv = resolve_window<NT, SUB, kPage, HW>(a, u, mrow, k0, wl, wlds, wave, lane, u.h - hl);
     // K tiles live in slots 0..3 of the first half of the ring, V tiles in the second
     // half; page p uses K slot p % 4 and V slot p % 4.
     auto k_slot = [&](int p) { return ring_addr + (uint32_t)(p % kRing) * kTileBytes; };
@@ -692,7 +715,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     // this wave's share of page p's K (is_v false) or V tile
     auto gather_tile = [&](int p, bool is_v) {
       if (!gatherer || p >= nv) return;
-      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]);
+      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]) & 0xFFFF;
       const uint16_t* sub_base[SUB];
 #pragma unroll
       for (int x = 0; x < SUB; ++x)
@@ -720,19 +743,29 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     for (int v = 0; v < nv; v += 2) {
       const bool has_b = v + 1 < nv;
       const int par = (v >> 1) & 1;
-      // ---- key sides (Eq. (1), (2), (5)): S^T, running max, partial margins
-      const int ja = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      // ---- key sides (Eq. (1), (2), (5)): S^T, running max, partial margins.  A head
+      //      takes no part in a visit outside its membership: no logits, no vote.
+      const int va = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      const bool mine_a = !MEMB || ((va >> (16 + hl)) & 1);
       f32x16_t acc_a[2], acc_b[2];
-      qk_tile(k_slot(v), qf, lane, acc_a);
-      const float mloc_a = mask_rowmax2(acc_a, ja, u.i, r_blk, u.L, lane >> 5, scale_log2);
+      float mloc_a = -INFINITY;
+      if (mine_a) {
+        qk_tile(k_slot(v), qf, lane, acc_a);
+        mloc_a = mask_rowmax2(acc_a, va & 0xFFFF, u.i, r_blk, u.L, lane >> 5, scale_log2);
+      }
       const float mnew_a = fmaxf(m2, mloc_a);
       const float dd_a = (row_ok && mloc_a != -INFINITY) ? (mloc_a - mnew_a) : -INFINITY;
       const float marg_a = max_lanes32(dd_a);
       float mnew_b = mnew_a, marg_b = -INFINITY;
+      bool mine_b = false;
       if (has_b) {
-        const int jb = __builtin_amdgcn_readfirstlane(wlds.vis_j[v + 1]);
-        qk_tile(k_slot(v + 1), qf, lane, acc_b);
-        const float mloc_b = mask_rowmax2(acc_b, jb, u.i, r_blk, u.L, lane >> 5, scale_log2);
+        const int vb = __builtin_amdgcn_readfirstlane(wlds.vis_j[v + 1]);
+        mine_b = !MEMB || ((vb >> (16 + hl)) & 1);
+        float mloc_b = -INFINITY;
+        if (mine_b) {
+          qk_tile(k_slot(v + 1), qf, lane, acc_b);
+          mloc_b = mask_rowmax2(acc_b, vb & 0xFFFF, u.i, r_blk, u.L, lane >> 5, scale_log2);
+        }
         mnew_b = fmaxf(mnew_a, mloc_b);
         const float dd_b = (row_ok && mloc_b != -INFINITY) ? (mloc_b - mnew_b) : -INFINITY;
         marg_b = max_lanes32(dd_b);
@@ -755,7 +788,8 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       gather_tile(v + 2, true);
       gather_tile(v + 3, true);
       // ---- value side of page 2k, then of page 2k+1
-      auto value_side = [&](int w, const f32x16_t (&acc)[2], float mnew, float marg, float partner) {
+      auto value_side = [&](int w, const f32x16_t (&acc)[2], float mnew, float marg, float partner, bool mine) {
+        if (!mine) return;  // not this head's entry: logged as not visited, state unchanged
         const float margin2 = fmaxf(marg, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(partner))));
         const bool skip = skip_on && (margin2 < tau2);
         if (logging && half == 0 && lane == 0) {
@@ -770,8 +804,8 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
           pv_tile(v_slot(w), pb, lane, o);
         }
       };
-      value_side(v, acc_a, mnew_a, marg_a, pa);
-      if (has_b) value_side(v + 1, acc_b, mnew_b, marg_b, pbv);
+      value_side(v, acc_a, mnew_a, marg_a, pa, mine_a);
+      if (has_b) value_side(v + 1, acc_b, mnew_b, marg_b, pbv, mine_b);
     }
     wait_vmcnt<0>();  // no page gather may still be writing LDS past this point
     __syncthreads();  // the window's LDS (visit list, ring, log) is reused next
@@ -795,7 +829,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
 // for the block), the barrier, then the value sides under one exponent base.
 // NPB: physical pages per logical block (128 / page_len); a 64-key tile spans SUB of
 // them, or lies in half of one 128-token page (NPB = 1, row offset 64 x).
-template <int HW, int NPB>
+template <int HW, int NPB, bool MEMB>
 __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const PrefillArgs a, int heads_per_group,
                                                                     int nsub) {
   constexpr int B = 2 * kPage;  // tokens per logical block
@@ -850,7 +884,7 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
     const int wl = min(kWindow, u.len - k0);
     if (logging && quarter == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
-    const int nv = resolve_window<NT, NPB, B>(a, u, mrow, k0, wl, wlds, wave, lane);
+    const int nv = resolve_window<NT, NPB, B, HW>(a, u, mrow, k0, wl, wlds, wave, lane, u.h - hl);
     const int ntiles = 2 * nv;
     auto k_slot = [&](int t) { return ring_addr + (uint32_t)(t % kRing) * kTileBytes; };
     auto v_slot = [&](int t) { return ring_addr + (uint32_t)(kRing * kTileBytes) + (uint32_t)(t % kRing) * kTileBytes; };
@@ -859,7 +893,7 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
     auto gather_tile = [&](int t, bool is_v) {
       if (!gatherer || t >= ntiles) return;
       const int blk = t >> 1;
-      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[blk]);
+      const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[blk]) & 0xFFFF;
       const int valid = u.L - (jp * B + (t & 1) * kPage);
       const int xs = valid > 0 ? (t & 1) : 0;
       const uint16_t* sub_base[SUB];
@@ -887,21 +921,26 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
     const bool vote = skip_on || logging;
     for (int v = 0; v < nv; ++v) {
       const int par = v & 1;
-      const int j = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      const int vj = __builtin_amdgcn_readfirstlane(wlds.vis_j[v]);
+      const int j = vj & 0xFFFF;
+      const bool mine = !MEMB || ((vj >> (16 + hl)) & 1);  // the block belongs to this head
       const int key0 = j * B;
       // ---- key side (Eq. (1), (2), (5)) over the block's 128 keys
       f32x16_t acc_a[2], acc_b[2];
-      qk_tile(k_slot(2 * v), qf, lane, acc_a);
-      qk_tile(k_slot(2 * v + 1), qf, lane, acc_b);
-      const bool diag = j == u.i;
-      mask_tile_at(acc_a, key0, c_tok, u.L, hi, diag || u.L - key0 < kPage);
-      mask_tile_at(acc_b, key0 + kPage, c_tok, u.L, hi, diag || u.L - key0 < B);
-      float mx = -INFINITY;
+      float mloc = -INFINITY;
+      if (mine) {
+        qk_tile(k_slot(2 * v), qf, lane, acc_a);
+        qk_tile(k_slot(2 * v + 1), qf, lane, acc_b);
+        const bool diag = j == u.i;
+        mask_tile_at(acc_a, key0, c_tok, u.L, hi, diag || u.L - key0 < kPage);
+        mask_tile_at(acc_b, key0 + kPage, c_tok, u.L, hi, diag || u.L - key0 < B);
+        float mx = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(acc_a[tt][e], acc_b[tt][e]));
-      const float mloc = permlane32_max(mx) * scale_log2;
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(acc_a[tt][e], acc_b[tt][e]));
+        mloc = mul_unfused(permlane32_max(mx), scale_log2);
+      }
       const float mnew = fmaxf(m2, mloc);
       const float dd = (row_ok && mloc != -INFINITY) ? (mloc - mnew) : -INFINITY;
       const float marg = max_lanes32(dd);
@@ -925,12 +964,12 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
       gather_tile(2 * v + 3, true);
       // ---- value side of the block: both tiles under one exponent base
       const bool skip = skip_on && (margin2 < tau2);
-      if (logging && quarter == 0 && lane == 0) {
+      if (mine && logging && quarter == 0 && lane == 0) {
         dec_lds[hl][wlds.vis_k[v] - k0] = skip ? 1 : 0;
         mar_lds[hl][wlds.vis_k[v] - k0] = margin2 * kLn2;
       }
       m2 = mnew;
-      if (!skip) {
+      if (mine && !skip) {
         maybe_rebase(m2, b2, l2, o);
         bf16x8_t pb[4];
         float rs = probs_tile(acc_a, scale_log2, b2, pb);
@@ -966,7 +1005,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     const int npb = 2 * kPage / a.page_len;
     auto launch = [&](auto hw_c, auto npb_c) {
       constexpr int H = decltype(hw_c)::value, N = decltype(npb_c)::value;
-      hipLaunchKernelGGL((osk_prefill_b128_kernel<H, N>), grid, dim3(256 * H), 0, stream, a, G, ns);
+      if (a.membership != nullptr)
+        hipLaunchKernelGGL((osk_prefill_b128_kernel<H, N, true>), grid, dim3(256 * H), 0, stream, a, G, ns);
+      else
+        hipLaunchKernelGGL((osk_prefill_b128_kernel<H, N, false>), grid, dim3(256 * H), 0, stream, a, G, ns);
     };
     auto by_npb = [&](auto hw_c) {
       if (npb == 1) launch(hw_c, std::integral_constant<int, 1>{});
@@ -982,7 +1024,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int sub = kPage / a.page_len;
   auto launch = [&](auto hw_c, auto sub_c) {
     constexpr int H = decltype(hw_c)::value, S = decltype(sub_c)::value;
-    hipLaunchKernelGGL((osk_prefill_ring_kernel<H, S>), grid, dim3(128 * H), 0, stream, a, G, nsub);
+    if (a.membership != nullptr)
+      hipLaunchKernelGGL((osk_prefill_ring_kernel<H, S, true>), grid, dim3(128 * H), 0, stream, a, G, nsub);
+    else
+      hipLaunchKernelGGL((osk_prefill_ring_kernel<H, S, false>), grid, dim3(128 * H), 0, stream, a, G, nsub);
   };
   auto by_sub = [&](auto hw_c) {
     if (sub == 1) launch(hw_c, std::integral_constant<int, 1>{});

@@ -100,17 +100,24 @@ def abort_count(db: DeviceBatch, workspace, max_mask_len: int) -> int:
 
 def prefill(db: DeviceBatch, order_mask, mask_len, delta: float, log: bool = False,
             outputs: Optional[PrefillOutputs] = None, workspace=None, stream=None,
-            sm_scale: float = 0.0) -> PrefillOutputs:
-    """One call of cosa_osk_prefill on device-resident inputs."""
+            sm_scale: float = 0.0, membership=None) -> PrefillOutputs:
+    """One call of cosa_osk_prefill (cosa_osk_prefill_union with a membership mask) on
+    device-resident inputs."""
     width = int(order_mask.shape[2])
     dims = db.dims(width, sm_scale)
     if outputs is None:
         outputs = allocate_outputs(db, width, log)
     if workspace is None:
         workspace = workspace_for(db, width)
-    binding.cosa_osk_prefill(dims, db.q, db.k_pool, db.v_pool, db.page_table, db.cu_seqlens, db.cu_qblocks,
-                             order_mask, mask_len, delta, outputs.out, outputs.lse, outputs.decisions,
-                             outputs.margins, workspace=workspace, stream=stream)
+    if membership is None:
+        binding.cosa_osk_prefill(dims, db.q, db.k_pool, db.v_pool, db.page_table, db.cu_seqlens, db.cu_qblocks,
+                                 order_mask, mask_len, delta, outputs.out, outputs.lse, outputs.decisions,
+                                 outputs.margins, workspace=workspace, stream=stream)
+    else:
+        binding.cosa_osk_prefill_union(dims, db.q, db.k_pool, db.v_pool, db.page_table, db.cu_seqlens,
+                                       db.cu_qblocks, order_mask, mask_len, membership, delta, outputs.out,
+                                       outputs.lse, outputs.decisions, outputs.margins, workspace=workspace,
+                                       stream=stream)
     return outputs
 
 
@@ -147,6 +154,24 @@ def build_kap_mask(db: DeviceBatch, stride: int, mode: int, budget: float, width
     binding.cosa_build_kap_mask(dims, db.q, db.k_pool, db.page_table, db.cu_seqlens, db.cu_qblocks, stride, mode,
                                 budget, om, ml, kap_scores=sc, hrm_flags=fl, workspace=workspace, stream=stream)
     return (om, ml, sc, fl) if outputs else (om, ml)
+
+
+def build_union_mask(db: DeviceBatch, budget1: float, flags: int = COSA_FORCE_FIRST | COSA_FORCE_DIAG,
+                     width: Optional[int] = None, workspace=None, stream=None):
+    """cosa_build_union_mask; returns (order_mask, mask_len, membership, head_len)."""
+    import torch
+    G = db.num_q_heads // db.num_kv_heads
+    if width is None:
+        width = binding.cosa_union_mask_width(db.max_blocks, G, budget1, flags)
+    dims = db.dims(width)
+    dev = db.q.device
+    om = torch.empty((db.total_qblocks, db.num_kv_heads, width), dtype=torch.int32, device=dev)
+    ml = torch.empty((db.total_qblocks, db.num_kv_heads), dtype=torch.int32, device=dev)
+    mem = torch.empty((db.total_qblocks, db.num_q_heads, width), dtype=torch.uint8, device=dev)
+    hl = torch.empty((db.total_qblocks, db.num_q_heads), dtype=torch.int32, device=dev)
+    binding.cosa_build_union_mask(dims, db.q, db.k_pool, db.page_table, db.cu_seqlens, db.cu_qblocks, budget1,
+                                  om, ml, mem, hl, flags=flags, workspace=workspace, stream=stream)
+    return om, ml, mem, hl
 
 
 def validate_mask(db: DeviceBatch, order_mask, mask_len, stream=None) -> np.ndarray:

@@ -168,6 +168,28 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same prefill with a page set per q head (PageWeaver notes, section 2.2: the q
+ * heads of a KV group traverse the union of their sets, and a membership mask keeps
+ * each head's softmax to its own pages).  order_mask row (qb, g) is the union in
+ * visit order; membership uint8 [total_qblocks, Hq, max_mask_len] (device, read
+ * only) marks with a nonzero byte the entries k < mask_len that belong to q head
+ * h of KV head g.  A head takes part in a visit -- logits, running max, skip vote,
+ * value side -- only at its own entries, so it sees its own blocks in the union's
+ * order; every other entry is logged COSA_DECISION_NOT_VISITED for it, margin NaN.
+ * A repeated id is not visited by any head (its first occurrence counts, whoever
+ * it belongs to), and an entry no head of a workgroup's heads owns is not gathered.
+ * All 1 membership gives exactly cosa_osk_prefill.  membership may be NULL only
+ * when max_mask_len == 0; otherwise every argument is as for cosa_osk_prefill.
+ */
+cosa_status_t cosa_osk_prefill_union(const cosa_osk_dims_t* dims,
+                                     const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* page_table, const int32_t* cu_seqlens,
+                                     const int32_t* cu_qblocks, const int32_t* order_mask,
+                                     const int32_t* mask_len, const uint8_t* membership, float budget2,
+                                     void* out, float* lse, uint8_t* decisions, float* margins,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Row width a computation-order mask built by cosa_build_order_mask needs:
  * the longest |F_i| + ceil(budget1 * |R_i| - 1e-3) over blocks i < max_blocks_per_seq
  * (F_i: forced pages, R_i: the other causal pages).  Host-only.  Returns -1 for
@@ -204,6 +226,39 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
                                     const int32_t* cu_qblocks, float budget1, uint32_t flags,
                                     int32_t* order_mask, int32_t* mask_len, float* proxy_scores,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Row width a union mask of cosa_build_union_mask needs: the longest
+ * min(i + 1, group * (|F_i| + ceil(budget1 * |R_i| - 1e-3))) over blocks
+ * i < max_blocks_per_seq (group = Hq / Hkv).  Host-only.  -1 for
+ * max_blocks_per_seq < 1 or group < 1. */
+int32_t cosa_union_mask_width(int32_t max_blocks_per_seq, int32_t group, float budget1, uint32_t flags);
+
+/* Workspace bytes cosa_build_union_mask needs: those of cosa_build_order_mask, then
+ * each q head's fp32 block means [total_qblocks, Hq, 128] and score rows
+ * [total_qblocks, Hq, max_blocks], each region padded to 256 bytes.  Host-only. */
+size_t cosa_build_union_mask_workspace_bytes(const cosa_osk_dims_t* dims);
+
+/*
+ * Per-q-head page sets from the mean-pooled proxy, as a union row per KV head with a
+ * membership mask (PageWeaver notes, section 2.2, union U_G and membership M; Eq. (3)
+ * gives the reuse ratio sum head_len / sum mask_len).  Each q head h selects its own
+ * set with the rule of cosa_build_order_mask applied to its own score
+ * qbar_h . kbar_j (qbar_h: the mean of q_h over the block's valid rows): the forced
+ * pages plus its top ceil(budget1 * |R_i| - 1e-3) by (score descending, id
+ * ascending).  Row (qb, g) lists the union of the group's sets in the order of the
+ * shared mask (group score descending, id ascending), -1 after; mask_len is the
+ * union's size.  membership uint8 [total_qblocks, Hq, max_mask_len]: 1 where entry k
+ * is in head h's set, 0 elsewhere (also past mask_len); head_len int32
+ * [total_qblocks, Hq]: each head's set size.  dims->max_mask_len must be >=
+ * cosa_union_mask_width(max_blocks, Hq / Hkv, budget1, flags); Hq / Hkv <= 32.
+ * The output feeds cosa_osk_prefill_union.
+ */
+cosa_status_t cosa_build_union_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                    const int32_t* page_table, const int32_t* cu_seqlens,
+                                    const int32_t* cu_qblocks, float budget1, uint32_t flags,
+                                    int32_t* order_mask, int32_t* mask_len, uint8_t* membership,
+                                    int32_t* head_len, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* Stage-1 selection modes of cosa_build_kap_mask. */
 #define COSA_KAP_FRACTION 0 /* K_i = ceil(budget * (i + 1) - 1e-3), at least 1            */

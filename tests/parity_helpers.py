@@ -63,8 +63,9 @@ def unit_rows(batch, units):
     return rows
 
 
-def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_log=True):
-    """Oracle replay vs the GPU result; returns a stats dict, asserts the bars."""
+def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_log=True, membership=None):
+    """Oracle replay vs the GPU result; returns a stats dict, asserts the bars.
+    membership: the per-q-head membership of the union rows (None: shared rows)."""
     q, k, v, pt, B = oracle_arrays(batch)
     Hq, Hkv = q.shape[1], k.shape[1]
     if units is None:
@@ -72,7 +73,7 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
     taus = block_thresholds(batch.cu_seqlens, delta, page_size=B)
     rep = ReplayDecisions(gpu["decisions"], taus) if "decisions" in gpu else None
     ref = osk_reference(q, k, v, pt, batch.cu_seqlens, order_mask, mask_len, delta, page_size=B,
-                        units=units, decision_override=rep)
+                        units=units, decision_override=rep, membership=membership)
     stats = {"units": len(units)}
     rows = unit_rows(batch, units)
     # ---- decisions and margins
@@ -94,6 +95,12 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
         stats["margin_max_err"] = float(err.max()) if err.size else 0.0
         assert (err <= MARGIN_ABS + MARGIN_REL * np.abs(rm[fin])).all(), stats["margin_max_err"]
         assert np.isnan(gpu["margins"][evaluated & (rd == NOT_VISITED)]).all()
+        # a head's first visit moves every row's running max from -inf to m_loc: its
+        # margin is exactly 0 (no rounding residue of the logit scaling)
+        gvis = gd != NOT_VISITED
+        has = gvis.any(axis=2)
+        first = np.take_along_axis(gpu["margins"], gvis.argmax(axis=2)[..., None], axis=2)[..., 0]
+        assert (first[has] == 0.0).all(), "first-visit margins are not exactly 0"
     elif require_log:
         raise AssertionError("decision log required")
     # ---- output
@@ -129,7 +136,7 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
     return stats
 
 
-def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4):
+def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4, membership=None):
     """A skip scale giving about `fraction` skipped visits on this batch, from the
     oracle's own (decision-independent) margins.  The threshold is put in the middle of
     a gap of at least 2e-3 between consecutive distinct margins (the split nearest the
@@ -137,7 +144,7 @@ def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4):
     without such a gap, at the plain quantile."""
     q, k, v, pt, B = oracle_arrays(batch)
     ref = osk_reference(q, k, v, pt, batch.cu_seqlens, order_mask, mask_len, -1.0, page_size=B,
-                        compute_output=False)
+                        compute_output=False, membership=membership)
     m = ref["margins"]
     lnL = np.zeros(m.shape[0])
     for s in range(len(batch.cu_seqlens) - 1):

@@ -185,3 +185,41 @@ def test_kap_builder_rejects_bad_arguments():
     assert call(dd=d128, stride=8, wsb=16) == UNSUPPORTED
     assert call(dd=d128, stride=48, wsb=16) == UNSUPPORTED
     assert call(stride=16, wsb=16) == WORKSPACE and call(stride=8, wsb=16) == WORKSPACE
+
+
+def test_union_mask_width_matches_oracle():
+    from oracle.maskref import union_mask_width
+    for mp, G, b1, flags in [(32, 4, 0.5, 3), (2048, 4, 0.1, 3), (100, 2, 0.3, FORCE_FIRST), (7, 8, 1.0, 0),
+                             (1, 4, 0.5, 3), (300, 1, 0.2, 3)]:
+        want = union_mask_width(mp, G, float(np.float32(b1)), flags)
+        assert binding.cosa_union_mask_width(mp, G, b1, flags) == want, (mp, G, b1, flags)
+    assert binding.cosa_union_mask_width(0, 4, 0.5, 3) == -1
+    assert binding.cosa_union_mask_width(8, 0, 0.5, 3) == -1
+
+
+def test_union_entry_points_reject_bad_arguments_before_launch():
+    L = binding.lib()
+    fake = 0x10000
+    d = good_dims()
+    ws = binding.cosa_osk_workspace_bytes(d)
+    # the union prefill needs a membership mask whenever rows have entries
+    assert L.cosa_osk_prefill_union(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, None, 1.0,
+                                    fake, None, None, None, fake, ws, None) == INVALID
+    # and otherwise checks as the prefill does (here: a workspace that is too small)
+    assert L.cosa_osk_prefill_union(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, fake, 1.0,
+                                    fake, None, None, None, fake, 0, None) == WORKSPACE
+    G = 4
+    width = binding.cosa_union_mask_width(64, G, 0.2, 3)
+    du = good_dims(max_mask_len=width)
+    need = binding.cosa_build_union_mask_workspace_bytes(du)
+    assert need > binding.cosa_build_order_mask_workspace_bytes(du)
+    def call(dd=du, b1=0.2, flags=3, mem=fake, hl=fake, wsb=need, work=fake):
+        return L.cosa_build_union_mask(ctypes.byref(dd), fake, fake, fake, fake, fake, b1, flags, fake, fake, mem, hl,
+                                       work, wsb, None)
+    assert call(mem=None) == INVALID
+    assert call(hl=None) == INVALID
+    assert call(b1=-0.5) == INVALID
+    assert call(flags=8) == INVALID
+    assert call(dd=good_dims(max_mask_len=width - 1)) == INVALID          # narrower than the union can be
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(dd=good_dims(num_q_heads=40 * 8, max_mask_len=64 * 40)) == UNSUPPORTED   # 40 heads per group
