@@ -210,7 +210,7 @@ def main():
     ap.add_argument("--workload", default="cfg4_128k_structured")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--mask", choices=["proxy", "kap"], default="proxy",
+    ap.add_argument("--mask", choices=["proxy", "kap", "union"], default="proxy",
                     help="skip-sweep: sweep with the mean-pooled proxy masks or with KAP masks (stride 16, "
                          "the workload's budget as the fixed fraction)")
     ap.add_argument("--mode", choices=["bench", "counters", "skip-sweep"], default="bench",
@@ -255,10 +255,25 @@ def main():
             om, ml = runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1)
         skip_sweep(args, wl, db, om, ml, args.mask)
         return
+    # the timed prefill's mask: the mean-pooled proxy (default), KAP at the workload's budget
+    # as the fixed fraction, or per-q-head sets as union rows with membership
+    membership = None
+    reuse = None
+    if args.mask == "kap":
+        om, ml = runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1)
+    elif args.mask == "union":
+        om, ml, membership, head_len = runner.build_union_mask(db, wl.budget1)
+        reuse = float(head_len.sum().item()) / float(ml.sum().item())
     width = om.shape[2]
-    ws_b = torch.empty(binding.cosa_build_order_mask_workspace_bytes(db.dims(width)), dtype=torch.uint8,
-                       device="cuda")
-    builder_ms, _ = time_calls(lambda: runner.build_mask(db, wl.budget1, workspace=ws_b), 5, 2)
+    if args.mask == "union":
+        ws_b = torch.empty(binding.cosa_build_union_mask_workspace_bytes(db.dims(width)), dtype=torch.uint8,
+                           device="cuda")
+        builder_ms, _ = time_calls(lambda: runner.build_union_mask(db, wl.budget1, workspace=ws_b), 5, 2)
+    else:
+        wb = binding.cosa_order_mask_width(db.max_blocks, wl.budget1)
+        ws_b = torch.empty(binding.cosa_build_order_mask_workspace_bytes(db.dims(wb)), dtype=torch.uint8,
+                           device="cuda")
+        builder_ms, _ = time_calls(lambda: runner.build_mask(db, wl.budget1, workspace=ws_b), 5, 2)
     kap_ms = None
     if db.num_q_heads // db.num_kv_heads * (db.block_size // KAP_STRIDE) <= 32:
         # the KAP builder (CoSA section 4.2): stride 16, fixed fraction = the workload's budget, and Top-p 0.95
@@ -272,7 +287,7 @@ def main():
         del ws_k
 
     # ---- one logged (untimed) call: visited / computed counts for the flop count
-    logged = runner.prefill(db, om, ml, delta, log=True)
+    logged = runner.prefill(db, om, ml, delta, log=True, membership=membership)
     torch.cuda.synchronize()
     dec = logged.decisions
     visited = int((dec != 2).sum().item())
@@ -285,7 +300,7 @@ def main():
     outs = runner.allocate_outputs(db, width, log=False)
     outs.lse = None
     ws = runner.workspace_for(db, width)
-    step = lambda: runner.prefill(db, om, ml, delta, outputs=outs, workspace=ws)
+    step = lambda: runner.prefill(db, om, ml, delta, outputs=outs, workspace=ws, membership=membership)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     per, wall = time_calls(step, args.steps, args.warmup)
     med = statistics.median(per)
@@ -321,7 +336,7 @@ def main():
 
     # ---- roofline of the dominant kernel
     traffic = None
-    tfile = TRAFFIC_FILES.get(wl.name)
+    tfile = TRAFFIC_FILES.get(wl.name) if args.mask == "proxy" else None  # counters taken with the proxy mask
     if tfile and os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
@@ -353,11 +368,12 @@ def main():
         "config": {"workload": wl.name, "seq_len": wl.seq_lens[0] if len(wl.seq_lens) == 1 else list(wl.seq_lens),
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": 128,
                    "page_size": int(batch.k_pool.shape[2]), "block_size": B, "budget1": wl.budget1,
-                   "skip_scale_delta": delta},
+                   "skip_scale_delta": delta, "mask": args.mask},
         "visited_q_head_pages": n_q_visits, "computed_q_head_pages": computed,
         "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
         "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
         "dense": dense, "mask_builder_ms": statistics.median(builder_ms), "kap_builder": kap_ms,
+        "reuse_ratio": reuse,
         "osk_plus_builder_ms": med + statistics.median(builder_ms),
         "roofline": roofline, "attainable": attain, "cpu_baseline": cpu, "aborted_workgroups": aborts,
     }
