@@ -30,6 +30,8 @@
 //               heads' candidates by their own scores mark each head's top n_keep,
 //               then one sort of the union by the group score writes the row.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -210,38 +212,72 @@ __device__ __forceinline__ uint64_t sort_key(float score, int id) {
   return ((uint64_t)(~ord) << 32) | (uint32_t)id;
 }
 
-// keys: dynamic LDS of the launch's key capacity (a power of two >= max_pages_per_seq)
-__global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
-  extern __shared__ uint64_t keys[];
-  __shared__ uint64_t fkeys[2];
-  const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
-  // block index within the sequence; the clamp keeps the candidate list inside the
-  // LDS key array even for a cu_qblocks inconsistent with max_pages_per_seq
-  const int i = min(qb - a.cu_qblocks[s], a.max_pages - 1);
-  const bool f_first = (a.flags & 1u) != 0u;
-  const bool f_diag = (a.flags & 2u) != 0u && !(f_first && i == 0);
-  const int nf = (f_first ? 1 : 0) + (f_diag ? 1 : 0);
-  const int nrest = i + 1 - nf;
-  const int nkeep = keep_count(a.budget1, nrest);
-  int N = 1;
-  while (N < nrest) N <<= 1;
-  const float* srow = a.score_rows + ((int64_t)qb * a.hkv + g) * a.max_pages;
-  for (int j = tid; j <= i; j += 256) {
-    const uint64_t key = sort_key(srow[j], j);
-    if (f_first && j == 0) fkeys[0] = key;
-    else if (f_diag && j == i) fkeys[f_first ? 1 : 0] = key;
-    else keys[j - ((f_first && j > 0) ? 1 : 0)] = key;
+// Radix select: for each of nh segments (segment seg holds n keys whose 64-bit value is
+// (hkey[seg * stride + r] << 32) | (r + r0), all distinct), the k-th smallest key (k >= 1,
+// k <= n) into s_prefix[seg], by eight 8-bit digit passes that all segments share.  Waves
+// 0 .. nh-1 of the NT threads search the digit histograms.  Called by every thread; ends
+// with a barrier.
+constexpr int kSelectMaxSegments = 8;
+template <int NT>
+__device__ __forceinline__ void radix_select(const uint32_t* hkey, int stride, int nh, int n, int r0, int k,
+                                             int (*hist)[256], uint64_t* s_prefix, int* s_k, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  if (tid < nh) {
+    s_prefix[tid] = 0ull;
+    s_k[tid] = k;
   }
-  if (a.scores)
-    for (int j = i + 1 + tid; j < a.max_pages; j += 256)
-      a.scores[((int64_t)qb * a.hkv + g) * a.max_pages + j] = __builtin_nanf("");
-  for (int x = nrest + tid; x < N; x += 256) keys[x] = ~0ull;
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int kk = 2; kk <= N; kk <<= 1) {
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+    for (int x = tid; x < nh * 256; x += NT) hist[x >> 8][x & 255] = 0;
+    __syncthreads();
+    for (int x = tid; x < nh * n; x += NT) {
+      const int seg = x / n, r = x - seg * n;
+      const uint64_t key = ((uint64_t)hkey[seg * stride + r] << 32) | (uint32_t)(r + r0);
+      if ((key & pmask) == (s_prefix[seg] & pmask)) atomicAdd(&hist[seg][(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (wave < nh) {
+      // the bin holding the segment's kk-th smallest remaining key; lane l sums bins 4l .. 4l+3
+      const int kk = s_k[wave];
+      const int c0 = hist[wave][4 * lane], c1 = hist[wave][4 * lane + 1];
+      const int c2 = hist[wave][4 * lane + 2], c3 = hist[wave][4 * lane + 3];
+      int incl = c0 + c1 + c2 + c3;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int excl = incl - (c0 + c1 + c2 + c3);
+      const uint64_t hit = __ballot(incl >= kk);
+      if (hit != 0ull && lane == __builtin_ctzll(hit)) {
+        int before = excl, b = 4 * lane;
+        if (before + c0 < kk) {
+          before += c0;
+          ++b;
+          if (before + c1 < kk) {
+            before += c1;
+            ++b;
+            if (before + c2 < kk) {
+              before += c2;
+              ++b;
+            }
+          }
+        }
+        s_prefix[wave] |= (uint64_t)b << shift;
+        s_k[wave] = kk - before;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Ascending bitonic sort of n (a power of two) keys in LDS by NT threads.
+template <int NT>
+__device__ __forceinline__ void bitonic_block(uint64_t* keys, int n, int tid) {
+  for (int kk = 2; kk <= n; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int x = tid; x < N; x += 256) {
+      for (int x = tid; x < n; x += NT) {
         const int y = x ^ jj;
         if (y > x) {
           const uint64_t p = keys[x], q = keys[y];
@@ -252,27 +288,58 @@ __global__ __launch_bounds__(256) void mask_select_kernel(const BuilderArgs a) {
       __syncthreads();
     }
   }
-  // merge the forced pages into the top nkeep
-  int32_t* row = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
-  uint64_t fk[2] = {nf > 0 ? fkeys[0] : ~0ull, nf > 1 ? fkeys[1] : ~0ull};
-  for (int x = tid; x < nkeep; x += 256) {
-    const uint64_t kx = keys[x];
-    int before = 0;
-    for (int f = 0; f < nf; ++f) before += (fk[f] < kx) ? 1 : 0;
-    row[x + before] = (int32_t)(kx & 0xffffffffu);
-  }
-  if (tid < nf) {
-    const uint64_t kx = fk[tid];
-    int lo = 0, hi = nkeep;  // number of selected keys below kx
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (keys[mid] < kx) lo = mid + 1; else hi = mid;
+}
+
+// One workgroup per (query block, KV head): the top n_keep of the non-forced candidates by
+// (score descending, id ascending) are found by a radix select on their keys, then the
+// kept and forced candidates -- n_keep + |F| keys -- are sorted by the same key.
+// dynamic LDS: [cap uint64: the kept keys][cap uint32: high key words of the candidates];
+// cap a power of two >= max_pages
+constexpr int kSelectThreads = 256;
+__global__ __launch_bounds__(kSelectThreads) void mask_select_kernel(const BuilderArgs a, int cap) {
+  extern __shared__ uint64_t keys[];
+  uint32_t* hkey = reinterpret_cast<uint32_t*>(keys + cap);
+  __shared__ int hist[1][256];
+  __shared__ uint64_t s_prefix[1];
+  __shared__ int s_k[1];
+  __shared__ int s_count;
+  const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int s = seq_of_qblock(a.cu_qblocks, a.num_seqs, qb);
+  // block index within the sequence; the clamp keeps the candidate list inside the
+  // LDS key array even for a cu_qblocks inconsistent with max_pages_per_seq
+  const int i = min(qb - a.cu_qblocks[s], a.max_pages - 1);
+  const bool f_first = (a.flags & 1u) != 0u;
+  const bool f_diag = (a.flags & 2u) != 0u && !(f_first && i == 0);
+  const int nf = (f_first ? 1 : 0) + (f_diag ? 1 : 0);
+  const int nrest = i + 1 - nf;
+  const int nkeep = keep_count(a.budget1, nrest);
+  const int r0 = f_first ? 1 : 0;  // rest index r is candidate id r + r0 (the diagonal is last)
+  const float* srow = a.score_rows + ((int64_t)qb * a.hkv + g) * a.max_pages;
+  for (int r = tid; r < nrest; r += kSelectThreads) hkey[r] = (uint32_t)(sort_key(srow[r + r0], 0) >> 32);
+  if (a.scores)
+    for (int j = i + 1 + tid; j < a.max_pages; j += kSelectThreads)
+      a.scores[((int64_t)qb * a.hkv + g) * a.max_pages + j] = __builtin_nanf("");
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  if (nkeep > 0 && nkeep < nrest) radix_select<kSelectThreads>(hkey, cap, 1, nrest, r0, nkeep, hist, s_prefix, s_k, tid);
+  // the kept keys and the forced ones, compacted (any order) and sorted
+  if (nkeep > 0)
+    for (int r = tid; r < nrest; r += kSelectThreads) {
+      const uint64_t key = ((uint64_t)hkey[r] << 32) | (uint32_t)(r + r0);
+      if (nkeep == nrest || key <= s_prefix[0]) keys[atomicAdd(&s_count, 1)] = key;
     }
-    const int other = (nf == 2 && fk[1 - tid] < kx) ? 1 : 0;
-    row[lo + other] = (int32_t)(kx & 0xffffffffu);
-  }
-  for (int x = nf + nkeep + tid; x < a.max_mask_len; x += 256) row[x] = -1;
-  if (tid == 0) a.mask_len[(int64_t)qb * a.hkv + g] = nf + nkeep;
+  if (tid == 0 && f_first) keys[atomicAdd(&s_count, 1)] = sort_key(srow[0], 0);
+  if (tid == 1 && f_diag) keys[atomicAdd(&s_count, 1)] = sort_key(srow[i], i);
+  __syncthreads();
+  const int n = nf + nkeep;
+  int N = 1;
+  while (N < n) N <<= 1;
+  for (int x = n + tid; x < N; x += kSelectThreads) keys[x] = ~0ull;
+  __syncthreads();
+  bitonic_block<kSelectThreads>(keys, N, tid);
+  int32_t* row = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
+  for (int x = tid; x < a.max_mask_len; x += kSelectThreads) row[x] = x < n ? (int32_t)(keys[x] & 0xffffffffu) : -1;
+  if (tid == 0) a.mask_len[(int64_t)qb * a.hkv + g] = n;
 }
 
 hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream) {
@@ -289,35 +356,33 @@ hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream) {
   // sort keys in LDS sized for the longest row (fewer workgroups per CU otherwise)
   int cap = 1;
   while (cap < a.max_pages) cap <<= 1;
-  hipLaunchKernelGGL(mask_select_kernel, grid, dim3(256), (size_t)cap * sizeof(uint64_t), stream, a);
+  hipLaunchKernelGGL(mask_select_kernel, grid, dim3(kSelectThreads), (size_t)cap * (sizeof(uint64_t) + sizeof(uint32_t)),
+                     stream, a, cap);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // union of per-q-head sets with membership
 // ---------------------------------------------------------------------------
-// ascending bitonic sort of n (a power of two) keys in LDS by the workgroup's 256 threads
-__device__ __forceinline__ void bitonic_lds(uint64_t* keys, int n, int tid) {
-  for (int kk = 2; kk <= n; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int x = tid; x < n; x += 256) {
-        const int y = x ^ jj;
-        if (y > x) {
-          const uint64_t p = keys[x], q = keys[y];
-          const bool up = (x & kk) == 0;
-          if ((p > q) == up) { keys[x] = q; keys[y] = p; }
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
+constexpr int kUnionThreads = 512;
+constexpr int kUnionMaxHeadsPerPass = kSelectMaxSegments;
 
-// dynamic LDS: keys [cap] uint64, then the candidates' head bits [cap] uint32 (bit hh:
-// candidate j is in head g*G + hh's set); cap a power of two >= max_pages
-__global__ __launch_bounds__(256) void union_select_kernel(const BuilderArgs a, int cap) {
-  extern __shared__ uint64_t keys[];
-  uint32_t* bits = reinterpret_cast<uint32_t*>(keys + cap);
+// One workgroup per (query block, KV head).  A head's set is its forced blocks plus the
+// n_keep smallest keys (score descending, id ascending) of its other candidates: the
+// n_keep-th smallest key is found exactly by a radix select over the 64-bit keys (eight
+// 8-bit passes, the heads of a pass sharing them), so no head's candidates are sorted;
+// only the union is sorted, by the group score.
+// dynamic LDS: [max(cap * 8, hpp * cap * 4) bytes: the heads' high key words, later the
+// union's sort keys][cap uint32: each candidate's head bits]; cap a power of two >= max_pages
+__global__ __launch_bounds__(kUnionThreads) void union_select_kernel(const BuilderArgs a, int cap, int hpp) {
+  extern __shared__ uint64_t dyn[];
+  const size_t region = max((size_t)cap, ((size_t)hpp * cap + 1) / 2);  // uint64 words
+  uint64_t* keys = dyn;                                        // union sort keys [cap]
+  uint32_t* hkey = reinterpret_cast<uint32_t*>(dyn);           // high key words [hpp][cap]
+  uint32_t* bits = reinterpret_cast<uint32_t*>(dyn + region);  // [cap]
+  __shared__ int hist[kUnionMaxHeadsPerPass][256];
+  __shared__ uint64_t s_prefix[kUnionMaxHeadsPerPass];
+  __shared__ int s_k[kUnionMaxHeadsPerPass];
   __shared__ int s_count;
   const int qb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int G = a.hq / a.hkv;
@@ -328,47 +393,53 @@ __global__ __launch_bounds__(256) void union_select_kernel(const BuilderArgs a, 
   const int nf = (f_first ? 1 : 0) + (f_diag ? 1 : 0);
   const int nrest = i + 1 - nf;
   const int nkeep = keep_count(a.budget1, nrest);
+  const int r0 = f_first ? 1 : 0;  // rest index r is candidate id r + r0 (the diagonal is last)
   const uint32_t all = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
-  auto forced = [&](int j) { return (f_first && j == 0) || (f_diag && j == i); };
-  for (int j = tid; j <= i; j += 256) bits[j] = forced(j) ? all : 0u;
+  for (int j = tid; j <= i; j += kUnionThreads)
+    bits[j] = ((f_first && j == 0) || (f_diag && j == i)) ? all : 0u;
   if (tid == 0) s_count = 0;
-  int N = 1;
-  while (N < nrest) N <<= 1;
-  // each head's top nkeep of the non-forced candidates by its own score
-  for (int hh = 0; hh < G; ++hh) {
-    const float* srow = a.head_score_rows + ((int64_t)qb * a.hq + g * G + hh) * a.max_pages;
-    __syncthreads();  // the previous head's reads of keys are done
-    for (int j = tid; j <= i; j += 256)
-      if (!forced(j)) keys[j - ((f_first && j > 0) ? 1 : 0)] = sort_key(srow[j], j);
-    for (int x = nrest + tid; x < N; x += 256) keys[x] = ~0ull;
+  for (int h0 = 0; h0 < G; h0 += hpp) {
+    const int nh = min(hpp, G - h0);
     __syncthreads();
-    bitonic_lds(keys, N, tid);
-    for (int x = tid; x < nkeep; x += 256) bits[(int)(keys[x] & 0xffffffffu)] |= 1u << hh;
+    for (int x = tid; x < nh * nrest; x += kUnionThreads) {
+      const int seg = x / nrest, r = x - seg * nrest;
+      const float sc = a.head_score_rows[((int64_t)qb * a.hq + g * G + h0 + seg) * a.max_pages + r + r0];
+      hkey[seg * cap + r] = (uint32_t)(sort_key(sc, 0) >> 32);
+    }
+    __syncthreads();
+    if (nkeep > 0 && nkeep < nrest)
+      radix_select<kUnionThreads>(hkey, cap, nh, nrest, r0, nkeep, hist, s_prefix, s_k, tid);
+    // members: the keys up to the n_keep-th smallest (all of them when n_keep == |R|)
+    if (nkeep > 0) {
+      for (int x = tid; x < nh * nrest; x += kUnionThreads) {
+        const int seg = x / nrest, r = x - seg * nrest;
+        const uint64_t key = ((uint64_t)hkey[seg * cap + r] << 32) | (uint32_t)(r + r0);
+        if (nkeep == nrest || key <= s_prefix[seg]) atomicOr(&bits[r + r0], 1u << (h0 + seg));
+      }
+    }
   }
   __syncthreads();
-  // the union, in the group score's order (score descending, id ascending)
-  int N2 = 1;
-  while (N2 < i + 1) N2 <<= 1;
+  // the union's members, compacted, then sorted by the group score (descending, id ascending)
   const float* grow = a.score_rows + ((int64_t)qb * a.hkv + g) * a.max_pages;
-  int mine = 0;
-  for (int j = tid; j < N2; j += 256) {
-    const bool in = j <= i && bits[j] != 0u;
-    keys[j] = in ? sort_key(grow[j], j) : ~0ull;
-    mine += in ? 1 : 0;
-  }
-  if (mine) atomicAdd(&s_count, mine);
+  for (int j = tid; j <= i; j += kUnionThreads)
+    if (bits[j] != 0u) keys[atomicAdd(&s_count, 1)] = sort_key(grow[j], j);
   __syncthreads();
-  bitonic_lds(keys, N2, tid);
-  const int nu = min(s_count, a.max_mask_len);
+  const int nu = s_count;
+  int N2 = 1;
+  while (N2 < nu) N2 <<= 1;
+  for (int x = nu + tid; x < N2; x += kUnionThreads) keys[x] = ~0ull;
+  __syncthreads();
+  bitonic_block<kUnionThreads>(keys, N2, tid);
+  const int nw = min(nu, a.max_mask_len);
   int32_t* row = a.order_mask + ((int64_t)qb * a.hkv + g) * a.max_mask_len;
-  for (int x = tid; x < a.max_mask_len; x += 256) {
-    const int id = x < nu ? (int)(keys[x] & 0xffffffffu) : -1;
+  for (int x = tid; x < a.max_mask_len; x += kUnionThreads) {
+    const int id = x < nw ? (int)(keys[x] & 0xffffffffu) : -1;
     row[x] = id;
     const uint32_t b = id >= 0 ? bits[id] : 0u;
     for (int hh = 0; hh < G; ++hh)
       a.membership[((int64_t)qb * a.hq + g * G + hh) * a.max_mask_len + x] = (uint8_t)((b >> hh) & 1u);
   }
-  if (tid == 0) a.mask_len[(int64_t)qb * a.hkv + g] = nu;
+  if (tid == 0) a.mask_len[(int64_t)qb * a.hkv + g] = nw;
   if (tid < G) a.head_len[(int64_t)qb * a.hq + g * G + tid] = nf + nkeep;
 }
 
@@ -390,8 +461,12 @@ hipError_t launch_build_union_mask(const BuilderArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   int cap = 1;
   while (cap < a.max_pages) cap <<= 1;
-  hipLaunchKernelGGL(union_select_kernel, grid, dim3(256), (size_t)cap * (sizeof(uint64_t) + sizeof(uint32_t)),
-                     stream, a, cap);
+  // heads selected together per pass: as many as fit their high key words in 32 KiB
+  const int G = a.hq / a.hkv;
+  const int hpp = max(1, min(min(G, kUnionMaxHeadsPerPass), (int)((32u << 10) / ((size_t)cap * 4))));
+  const size_t region = std::max((size_t)cap, ((size_t)hpp * cap + 1) / 2) * sizeof(uint64_t);
+  hipLaunchKernelGGL(union_select_kernel, grid, dim3(kUnionThreads), region + (size_t)cap * sizeof(uint32_t), stream,
+                     a, cap, hpp);
   return hipGetLastError();
 }
 
