@@ -15,9 +15,9 @@
 //   score  one workgroup per 8 consecutive query blocks of a sequence and a KV
 //          head: fp32 scores of the causal pages, each pooled key row read once
 //          for the 8 blocks; rows go to the caller's proxy_scores or workspace.
-//   select one workgroup per (query block, KV head): forced pages set aside, a
-//          bitonic sort of the rest by (score desc, id asc) in LDS, and a merge of
-//          the forced pages into the top n_keep by the same key.
+//   select one workgroup per (query block, KV head): a radix select finds the
+//          n_keep-th key of the non-forced candidates by (score desc, id asc); the
+//          kept and forced keys are then bitonic-sorted in LDS.
 //
 // Per-q-head sets (PageWeaver notes, section 2.2: the heads of a group traverse the
 // union of their sets, a membership mask keeping each head to its own): each q head
@@ -26,9 +26,10 @@
 // the shared mask, with membership[qb, h, k] = 1 iff entry k is in head h's set.
 //   pool_heads  one workgroup per (query block, KV head): the G per-head means;
 //   score       the score kernel above over per-head rows;
-//   union       one workgroup per (query block, KV head): G bitonic sorts of the
-//               heads' candidates by their own scores mark each head's top n_keep,
-//               then one sort of the union by the group score writes the row.
+//   union       one workgroup per (query block, KV head): a radix select over the
+//               G heads' candidates (their own scores; the heads share the digit
+//               passes) marks each head's top n_keep, then one sort of the union's
+//               members by the group score writes the row.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -1,14 +1,19 @@
 // Ordered-skipping block-sparse prefill attention for gfx950 (MI355X).
 //
 // Method: CoSA section 4.3 and Appendix C, Algorithm A (attention loop): each
-// 64-row query block walks the logical pages of its computation-order mask in
-// mask order through the page table, keeps the tiled online softmax of section
-// 3.1 Eq. (1)-(2), and skips the value side of a page when Delta > 0 and
-// max_r(m_loc[r] - m[r]) < ln(Delta / N) (section 3.3, Eq. (5)), with the
-// running max m updated before the test.  Query/key visibility follows the
-// PageWeaver notes, section 2.1, Eq. (1): t < L and t <= c.
+// query block walks the logical blocks of its computation-order mask in mask order
+// through the page table, keeps the tiled online softmax of section 3.1 Eq. (1)-(2),
+// and skips the value side of a block when Delta > 0 and max_r(m_loc[r] - m[r]) <
+// ln(Delta / N) (section 3.3, Eq. (5)), with the running max m updated before the
+// test.  Query/key visibility follows the PageWeaver notes, section 2.1, Eq. (1):
+// t < L and t <= c.  Logical blocks hold 64 tokens (osk_prefill_ring_kernel) or 128
+// (osk_prefill_b128_kernel; CoSA Appendix D.1: one vote per 128-row query tile), each
+// resolved through the physical pages of the KV cache; with a membership mask the
+// q heads of a KV group keep their own block sets inside the union row (PageWeaver
+// notes, section 2.2).
 //
-// Organisation on the chip:
+// Organisation on the chip (64-token blocks; the 128-token kernel below differs as
+// its own comment says):
 // * one workgroup = one (query block, KV head[, head subgroup]) unit with HW q
 //   heads of the KV head's group; two waves per head, each owning 32 of the
 //   block's 64 query rows (2*HW waves, two waves per SIMD at HW = 4, so one

@@ -1,4 +1,4 @@
-"""Logical 64-token blocks over a KV cache paged at a smaller physical page size.
+"""Logical blocks (64 or 128 tokens) over a KV cache paged at another physical page size.
 
 TEST INFRASTRUCTURE ONLY (see oracle/osk.py).
 
