@@ -46,10 +46,16 @@ TRAFFIC_FILES = {
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and blank space are left out, so that
+    only a change of the code itself invalidates the stored counter summaries."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
