@@ -214,6 +214,8 @@ def osk_reference(q, k_pool, v_pool, page_table, cu_seqlens, order_mask, mask_le
     for (s, g), blocks in todo.items():
         t0 = int(cu_seqlens[s])
         L = int(cu_seqlens[s + 1] - cu_seqlens[s])
+        if L == 0 or len(blocks) == 0:
+            continue  # an empty sequence has no query blocks
         n_pages = -(-L // P)
         tau = skip_threshold(delta, L)
         heads = np.arange(g * G, (g + 1) * G)
@@ -372,6 +374,8 @@ def block_thresholds(cu_seqlens, delta: float, page_size: int = 64) -> np.ndarra
     taus = []
     for s in range(len(cu_seqlens) - 1):
         L = int(cu_seqlens[s + 1] - cu_seqlens[s])
+        if L == 0:
+            continue  # no query blocks
         t = skip_threshold(delta, L)
         taus += [np.nan if t is None else t] * (-(-L // page_size))
     return np.array(taus, dtype=np.float64)

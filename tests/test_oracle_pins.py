@@ -309,3 +309,25 @@ def test_replay_flip_at_near_tie_and_disagreement_elsewhere():
     res = osk_reference(q, k, v, pt, cu, om, ml, delta=delta, page_size=4, sm_scale=1.0, decision_override=rep)
     assert len(rep.disagreements) == 1 and rep.near_tie_flips == 0
     assert res["decisions"][1, 0, 1] == NOT_COMPUTED_SKIP
+
+
+def test_empty_sequence_in_a_packed_batch_changes_nothing_else():
+    """An empty sequence has no query blocks: packing one between two others leaves their
+    outputs, LSE, decisions and margins exactly as without it, and brute force agrees."""
+    rng = np.random.default_rng(41)
+    lens = [64 * 3 + 9, 70]
+    q, k, v, pt, cu = make_problem(rng, lens, 4, 2, 32, 64)
+    om, ml = random_masks(rng, lens, 2, 64, 6)
+    delta = 100.0
+    base = osk.osk_reference(q, k, v, pt, cu, om, ml, delta)
+    # the same tokens with an empty sequence in between (its page-table row all -1)
+    cu_e = np.array([0, cu[1], cu[1], cu[2]])
+    pt_e = np.full((3, pt.shape[1]), -1, dtype=pt.dtype)
+    pt_e[0], pt_e[2] = pt[0], pt[1]
+    res = osk.osk_reference(q, k, v, pt_e, cu_e, om, ml, delta)
+    for key in ("out", "lse", "decisions", "margins"):
+        np.testing.assert_array_equal(res[key], base[key])
+    np.testing.assert_array_equal(block_thresholds(cu_e, delta), block_thresholds(cu, delta))
+    out_bf, _ = osk.brute_force_attention(q, k, v, pt_e, cu_e, om, ml)
+    nos = osk.osk_reference(q, k, v, pt_e, cu_e, om, ml, -1.0)
+    np.testing.assert_allclose(nos["out"], out_bf, atol=1e-12)
