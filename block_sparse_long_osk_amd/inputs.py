@@ -193,6 +193,10 @@ def _gen_sequence(wl: Workload, seed: int, L: int):
     v *= inv
     n_pages = -(-L // PAGE)
     salient = np.zeros((Hkv, 0), dtype=np.int64)
+    if L == 0:  # an empty sequence: nothing to draw structure for
+        if wl.generator not in ("iid", "structured"):
+            raise ValueError(wl.generator)
+        return q, k, v, salient
     if wl.generator == "iid":
         k *= inv
     elif wl.generator == "structured":

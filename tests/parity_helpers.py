@@ -148,7 +148,9 @@ def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4, membershi
     m = ref["margins"]
     lnL = np.zeros(m.shape[0])
     for s in range(len(batch.cu_seqlens) - 1):
-        lnL[batch.cu_qblocks[s]:batch.cu_qblocks[s + 1]] = math.log(batch.cu_seqlens[s + 1] - batch.cu_seqlens[s])
+        L = int(batch.cu_seqlens[s + 1] - batch.cu_seqlens[s])
+        if L > 0:  # an empty sequence has no query blocks
+            lnL[batch.cu_qblocks[s]:batch.cu_qblocks[s + 1]] = math.log(L)
     x = np.sort((m + lnL[:, None, None])[np.isfinite(m)])
     kq = int(round(fraction * x.size))
     splits = np.flatnonzero(np.diff(x) > 2e-3) + 1      # x[k-1] < x[k] - 2e-3
