@@ -210,8 +210,8 @@ def skip_sweep(args, wl, db, om, ml, mask_kind="proxy"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--workload", default="cfg4_128k_structured")
     ap.add_argument("--no-cpu", action="store_true")
