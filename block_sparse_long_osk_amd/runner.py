@@ -38,6 +38,7 @@ class DeviceBatch:
         return -(-self.page_table.shape[1] * self.k_pool.shape[2] // self.block_size)
 
     def dims(self, max_mask_len: int, sm_scale: float = 0.0) -> binding.CosaOskDims:
+        """Dims of the batch with rows of max_mask_len entries; sm_scale <= 0 selects 1/sqrt(128)."""
         return binding.make_dims(self.q, self.k_pool, self.page_table, self.total_qblocks, max_mask_len,
                                  sm_scale=sm_scale, block_size=self.block_size)
 
@@ -139,13 +140,13 @@ def build_mask(db: DeviceBatch, budget1: float, flags: int = COSA_FORCE_FIRST | 
 
 
 def build_kap_mask(db: DeviceBatch, stride: int, mode: int, budget: float, width: Optional[int] = None,
-                   outputs: bool = False, workspace=None, stream=None):
+                   outputs: bool = False, workspace=None, stream=None, sm_scale: float = 0.0):
     """cosa_build_kap_mask on the device batch; returns (order_mask, mask_len[, scores, flags])."""
     import torch
     max_pages = db.max_blocks
     if width is None:
         width = binding.cosa_kap_mask_width(max_pages, mode, budget)
-    dims = db.dims(width)
+    dims = db.dims(width, sm_scale)
     dev = db.q.device
     om = torch.empty((db.total_qblocks, db.num_kv_heads, width), dtype=torch.int32, device=dev)
     ml = torch.empty((db.total_qblocks, db.num_kv_heads), dtype=torch.int32, device=dev)

@@ -61,8 +61,10 @@ def gather_sampled_keys(k_pool, pt_row, L: int, g: int, stride: int, page_size: 
     return np.asarray(k_pool[pages, g, toks % page_size, :], dtype=np.float64)
 
 
-def block_ranking(qs: np.ndarray, ks: np.ndarray, i: int, stride: int, page_size: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Eq. (8)-(12) for query block i of one q head.
+def block_ranking(qs: np.ndarray, ks: np.ndarray, i: int, stride: int, page_size: int,
+                  sm_scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Eq. (8)-(12) for query block i of one q head (logit scale sm_scale, 1/sqrt(d) by
+    default).
 
     qs: Q~ [R, d] and ks: K~ [R, d] of the sequence (float64).  Returns
     (s [i+1], hmax [i+1]): the block scores of Eq. (11) over this head's sampled
@@ -75,7 +77,10 @@ def block_ranking(qs: np.ndarray, ks: np.ndarray, i: int, stride: int, page_size
     if rows.size == 0:
         return np.zeros(i + 1), np.zeros(i + 1)
     ncols = min((i + 1) * per, R)                    # every key sample a row of block i may see
-    x = qs[rows] @ ks[:ncols].T / math.sqrt(d)       # Q~ K~^T / sqrt(d)
+    if sm_scale is None or sm_scale <= 0:
+        x = qs[rows] @ ks[:ncols].T / math.sqrt(d)   # Q~ K~^T / sqrt(d)
+    else:
+        x = (qs[rows] @ ks[:ncols].T) * sm_scale     # the caller's logit scale
     cols = np.arange(ncols)
     x = np.where(cols[None, :] <= rows[:, None], x, -np.inf)    # causal mask on samples
     x = x - x.max(axis=1, keepdims=True)
@@ -118,7 +123,7 @@ def mask_width(max_pages: int, mode: int, budget: float) -> int:
 
 def build_kap_mask(q, k_pool, page_table, cu_seqlens, num_kv_heads: int, stride: int, mode: int, budget: float,
                    page_size: int = 64, width: Optional[int] = None, blocks: Optional[List[int]] = None,
-                   return_hmax: bool = False):
+                   return_hmax: bool = False, sm_scale: Optional[float] = None):
     """KAP mask of every (query block, KV head), or of the global query blocks listed.
 
     Returns order_mask [nqb, Hkv, width] int32 (-1 padded), mask_len [nqb, Hkv],
@@ -161,7 +166,7 @@ def build_kap_mask(q, k_pool, page_table, cu_seqlens, num_kv_heads: int, stride:
                 s_row = np.zeros(i + 1)
                 hmax = np.zeros(i + 1)
                 for hh in range(G):
-                    s_h, m_h = block_ranking(qh[hh], ks, i, stride, page_size)
+                    s_h, m_h = block_ranking(qh[hh], ks, i, stride, page_size, sm_scale)
                     s_row += s_h
                     hmax = np.maximum(hmax, m_h)
                 h_row = (hmax == 1.0)

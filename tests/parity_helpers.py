@@ -63,7 +63,8 @@ def unit_rows(batch, units):
     return rows
 
 
-def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_log=True, membership=None):
+def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_log=True, membership=None,
+                  sm_scale=None):
     """Oracle replay vs the GPU result; returns a stats dict, asserts the bars.
     membership: the per-q-head membership of the union rows (None: shared rows)."""
     q, k, v, pt, B = oracle_arrays(batch)
@@ -73,7 +74,7 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
     taus = block_thresholds(batch.cu_seqlens, delta, page_size=B)
     rep = ReplayDecisions(gpu["decisions"], taus) if "decisions" in gpu else None
     ref = osk_reference(q, k, v, pt, batch.cu_seqlens, order_mask, mask_len, delta, page_size=B,
-                        units=units, decision_override=rep, membership=membership)
+                        units=units, decision_override=rep, membership=membership, sm_scale=sm_scale)
     stats = {"units": len(units)}
     rows = unit_rows(batch, units)
     # ---- decisions and margins
@@ -136,7 +137,7 @@ def check_prefill(batch, order_mask, mask_len, delta, gpu, units=None, require_l
     return stats
 
 
-def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4, membership=None):
+def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4, membership=None, sm_scale=None):
     """A skip scale giving about `fraction` skipped visits on this batch, from the
     oracle's own (decision-independent) margins.  The threshold is put in the middle of
     a gap of at least 2e-3 between consecutive distinct margins (the split nearest the
@@ -144,7 +145,7 @@ def delta_for_skip_fraction(batch, order_mask, mask_len, fraction=0.4, membershi
     without such a gap, at the plain quantile."""
     q, k, v, pt, B = oracle_arrays(batch)
     ref = osk_reference(q, k, v, pt, batch.cu_seqlens, order_mask, mask_len, -1.0, page_size=B,
-                        compute_output=False, membership=membership)
+                        compute_output=False, membership=membership, sm_scale=sm_scale)
     m = ref["margins"]
     lnL = np.zeros(m.shape[0])
     for s in range(len(batch.cu_seqlens) - 1):

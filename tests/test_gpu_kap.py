@@ -42,11 +42,11 @@ def expected_row(s, h, n):
     return ids[np.lexsort((ids, -s.astype(np.float64), -h.astype(np.int64)))][:n]
 
 
-def check_kap(rt, name, batch, stride, mode, budget, blocks=None):
+def check_kap(rt, name, batch, stride, mode, budget, blocks=None, sm_scale=None):
     import torch
     Hkv = batch.k_pool.shape[1]
     db = rt.upload(batch)
-    om_d, ml_d, sc_d, fl_d = rt.build_kap_mask(db, stride, mode, budget, outputs=True)
+    om_d, ml_d, sc_d, fl_d = rt.build_kap_mask(db, stride, mode, budget, outputs=True, sm_scale=sm_scale or 0.0)
     torch.cuda.synchronize()
     om_g, ml_g = om_d.cpu().numpy(), ml_d.cpu().numpy()
     sc_g, fl_g = sc_d.cpu().numpy(), fl_d.cpu().numpy()
@@ -55,7 +55,7 @@ def check_kap(rt, name, batch, stride, mode, budget, blocks=None):
     want = list(range(nqb)) if blocks is None else list(blocks)
     om_o, ml_o, sc_o, fl_o, hm_o = kap.build_kap_mask(q, k, pt, batch.cu_seqlens, Hkv, stride, mode, budget,
                                                       page_size=B, width=om_g.shape[2], blocks=want,
-                                                      return_hmax=True)
+                                                      return_hmax=True, sm_scale=sm_scale)
     starts = np.cumsum([0] + [-(-int(L) // B) for L in np.diff(batch.cu_seqlens)])
     stats = dict(units=0, flag_ties=0, len_ties=0, max_score_err=0.0)
     for pos, qb in enumerate(want):

@@ -46,6 +46,22 @@ def test_one_sample_per_block_is_exp_of_score_gap():
         assert fl[i, 0, : i + 1].sum() == 1
 
 
+def test_caller_scale_replaces_inverse_sqrt_d():
+    # the same one-sample-per-block closed form with a caller's logit scale s in place
+    # of 1/sqrt(d): Pbar[i, j] = exp(s (x_ij - max_j' x_ij')); s = 1/sqrt(d) is the default
+    L = 64 * 7
+    q, k, pt, cu = rand_case(L, 1, 1, 5)
+    x = raw_scores(q, k, pt, 0, 0, 64, L)
+    s = 0.25
+    _, _, sc, _ = kap.build_kap_mask(q, k, pt, cu, 1, 64, kap.MODE_FRACTION, 1.0, sm_scale=s)
+    for i in range(7):
+        xi = x[i, : i + 1]
+        np.testing.assert_allclose(sc[i, 0, : i + 1], np.exp(s * (xi - xi.max())), rtol=1e-12, atol=1e-15)
+    _, _, a, _ = kap.build_kap_mask(q, k, pt, cu, 1, 64, kap.MODE_FRACTION, 1.0)
+    _, _, b, _ = kap.build_kap_mask(q, k, pt, cu, 1, 64, kap.MODE_FRACTION, 1.0, sm_scale=1.0 / math.sqrt(D))
+    np.testing.assert_allclose(a, b, rtol=1e-14, atol=0)
+
+
 @pytest.mark.parametrize("stride", [16, 8])
 def test_hrm_flags_are_the_blocks_holding_row_maxima(stride):
     L, hq, hkv = 64 * 7 + 20, 4, 2
