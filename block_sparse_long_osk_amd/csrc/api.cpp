@@ -360,9 +360,24 @@ static size_t kap_flag_bytes(const cosa_osk_dims_t* d) {
   return round_up((size_t)d->total_qblocks * d->num_kv_heads * (size_t)std::max(max_blocks(d), 0) + 1);
 }
 
+// then the row-maximum codes, [total_qblocks, Hkv, G * samples per block] uint32, sized
+// for the largest sample count (8 per block)
+static size_t kap_rowmax_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->total_qblocks * (size_t)std::max(d->num_q_heads, 0) * 8 * sizeof(uint32_t) + 1);
+}
+
+// then the packed sampled-key tiles, [Hkv, slots] x 8 KiB with slots = total_qblocks *
+// samples per block / 32 + num_seqs, sized for 8 samples per block
+static int64_t kap_tile_slots(const cosa_osk_dims_t* d, int per) {
+  return (int64_t)d->total_qblocks * per / 32 + std::max(d->num_seqs, 0);
+}
+static size_t kap_tile_bytes(const cosa_osk_dims_t* d) {
+  return round_up((size_t)d->num_kv_heads * (size_t)kap_tile_slots(d, 8) * 8 * 64 * 16 + 1);
+}
+
 size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims) {
   if (dims == nullptr || dims->total_qblocks < 0 || dims->num_kv_heads < 1) return 0;
-  return kap_score_bytes(dims) + kap_flag_bytes(dims);
+  return kap_score_bytes(dims) + kap_flag_bytes(dims) + kap_rowmax_bytes(dims) + kap_tile_bytes(dims);
 }
 
 cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
@@ -404,6 +419,11 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   a.score_rows = kap_scores != nullptr ? kap_scores : static_cast<float*>(workspace);
   a.flag_rows = hrm_flags != nullptr ? hrm_flags
                                      : reinterpret_cast<uint8_t*>(static_cast<char*>(workspace) + kap_score_bytes(dims));
+  a.row_max = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kap_score_bytes(dims) + kap_flag_bytes(dims));
+  a.k_tiles = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kap_score_bytes(dims) + kap_flag_bytes(dims) +
+                                          kap_rowmax_bytes(dims));
+  if (kap_tile_slots(dims, blk / stride) > 0x7fffffff) return COSA_ERR_UNSUPPORTED;
+  a.tile_slots = (int32_t)kap_tile_slots(dims, blk / stride);
   a.q_st = dims->q_stride_tok;
   a.q_sh = dims->q_stride_head;
   a.kv_sp = dims->kv_stride_page;

@@ -1,0 +1,88 @@
+// Workgroup-wide selection and sorting of 64-bit keys in LDS, shared by the
+// computation-order mask builders (device code only: included by the .hip sources).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cosa_osk {
+
+// Radix select: for each of nh segments (segment seg holds n keys whose 64-bit value is
+// (hkey[seg * stride + r] << 32) | (r + r0), all distinct), the k-th smallest key (k >= 1,
+// k <= n) into s_prefix[seg], by eight 8-bit digit passes that all segments share.  Waves
+// 0 .. nh-1 of the NT threads search the digit histograms.  Called by every thread; ends
+// with a barrier.
+constexpr int kSelectMaxSegments = 8;
+template <int NT>
+__device__ __forceinline__ void radix_select(const uint32_t* hkey, int stride, int nh, int n, int r0, int k,
+                                             int (*hist)[256], uint64_t* s_prefix, int* s_k, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  if (tid < nh) {
+    s_prefix[tid] = 0ull;
+    s_k[tid] = k;
+  }
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+    for (int x = tid; x < nh * 256; x += NT) hist[x >> 8][x & 255] = 0;
+    __syncthreads();
+    for (int x = tid; x < nh * n; x += NT) {
+      const int seg = x / n, r = x - seg * n;
+      const uint64_t key = ((uint64_t)hkey[seg * stride + r] << 32) | (uint32_t)(r + r0);
+      if ((key & pmask) == (s_prefix[seg] & pmask)) atomicAdd(&hist[seg][(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (wave < nh) {
+      // the bin holding the segment's kk-th smallest remaining key; lane l sums bins 4l .. 4l+3
+      const int kk = s_k[wave];
+      const int c0 = hist[wave][4 * lane], c1 = hist[wave][4 * lane + 1];
+      const int c2 = hist[wave][4 * lane + 2], c3 = hist[wave][4 * lane + 3];
+      int incl = c0 + c1 + c2 + c3;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const int excl = incl - (c0 + c1 + c2 + c3);
+      const uint64_t hit = __ballot(incl >= kk);
+      if (hit != 0ull && lane == __builtin_ctzll(hit)) {
+        int before = excl, b = 4 * lane;
+        if (before + c0 < kk) {
+          before += c0;
+          ++b;
+          if (before + c1 < kk) {
+            before += c1;
+            ++b;
+            if (before + c2 < kk) {
+              before += c2;
+              ++b;
+            }
+          }
+        }
+        s_prefix[wave] |= (uint64_t)b << shift;
+        s_k[wave] = kk - before;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Ascending bitonic sort of n (a power of two) keys in LDS by NT threads.
+template <int NT>
+__device__ __forceinline__ void bitonic_block(uint64_t* keys, int n, int tid) {
+  for (int kk = 2; kk <= n; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int x = tid; x < n; x += NT) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const uint64_t p = keys[x], q = keys[y];
+          const bool up = (x & kk) == 0;
+          if ((p > q) == up) { keys[x] = q; keys[y] = p; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace cosa_osk

@@ -93,6 +93,9 @@ struct KapArgs {
   uint8_t* flags_out;   // nullable: the caller's copy of the HRM flags
   float* score_rows;    // [total_qblocks, hkv, max_pages]: scores_out, or workspace
   uint8_t* flag_rows;   // [total_qblocks, hkv, max_pages]: flags_out, or workspace
+  uint32_t* row_max;    // workspace: [total_qblocks, hkv, G * block / stride] row-maximum codes
+  uint16_t* k_tiles;    // workspace: [hkv, tile_slots] packed key tiles (8 KiB each)
+  int32_t tile_slots;   // total_qblocks * (block / stride) / 32 + num_seqs
   int64_t q_st, q_sh, kv_sp, kv_sh, kv_st;
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
   int32_t pt_stride, page_len, block;

@@ -271,8 +271,10 @@ cosa_status_t cosa_build_union_mask(const cosa_osk_dims_t* dims, const void* q, 
 int32_t cosa_kap_mask_width(int32_t max_blocks_per_seq, int32_t mode, float budget);
 
 /* Workspace bytes cosa_build_kap_mask needs: fp32 block scores and uint8 HRM flags
- * [total_qblocks, Hkv, max_blocks] each, each region padded to 256 bytes
- * (used where the caller passes no array of its own).  Host-only. */
+ * [total_qblocks, Hkv, max_blocks] each (used where the caller passes no array of
+ * its own), then the sampled rows' maxima, total_qblocks * Hq * 8 uint32, then a copy
+ * of the sampled keys, Hkv * (total_qblocks / 4 + num_seqs) tiles of 8 KiB; each
+ * region padded to 256 bytes.  Host-only. */
 size_t cosa_build_kap_mask_workspace_bytes(const cosa_osk_dims_t* dims);
 
 /*

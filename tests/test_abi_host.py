@@ -162,7 +162,9 @@ def test_kap_builder_rejects_bad_arguments():
     d = good_dims(max_mask_len=64)
     fake = 0x10000
     need = binding.cosa_build_kap_mask_workspace_bytes(d)
-    assert need >= 64 * 8 * 64 * 5
+    # scores and flags [64 query blocks, 8 KV heads, 64 blocks], uint32 row maxima of 32 q
+    # heads x up to 8 sampled rows per query block, 8 KV heads x (64 / 4 + 1) key tiles
+    assert need >= 64 * 8 * 64 * 5 + 64 * 32 * 8 * 4 + 8 * (64 // 4 + 1) * 8192
     def call(dd=d, stride=16, mode=0, b=0.3, wsb=need, work=fake):
         return L.cosa_build_kap_mask(ctypes.byref(dd), fake, fake, fake, fake, fake, stride, mode, b, fake, fake,
                                      None, None, work, wsb, None)
