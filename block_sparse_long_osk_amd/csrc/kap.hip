@@ -49,6 +49,11 @@ constexpr float kKapLog2e = 1.442695040888963407f;
 #endif
 constexpr int kKapColumnTiles = KAP_COLUMN_TILES;  // column tiles of 32 query rows per wave
 
+// x * y rounded by itself (never contracted into a following add or subtract)
+__device__ __forceinline__ float kap_mul_unfused(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
 __device__ __forceinline__ float kap_partner_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -282,7 +287,8 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int chun
   const float scale = a.sm_scale;  // > 0
   float M[CT];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) M[ct] = w.row_ok[ct] ? ord_float(a.row_max[w.row_index(a, ct)]) * scale : -INFINITY;
+  for (int ct = 0; ct < CT; ++ct)
+    M[ct] = w.row_ok[ct] ? kap_mul_unfused(ord_float(a.row_max[w.row_index(a, ct)]), scale) : -INFINITY;
   for (int kt = w.t_begin; kt < w.t_end; ++kt) {
     kf32x16_t acc[CT];
     w.tile(a, kt, acc);
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const KapArgs a, int chun
             if (w.key_of(kt, e) <= w.r[ct]) mb = fmaxf(mb, acc[ct][e]);
         }
         if (PER == 8) mb = kap_partner_max(mb);
-        mb *= scale;
+        mb = kap_mul_unfused(mb, scale);  // rounded as M was: Pbar is exactly 1 at the row maximum
         const int j = PER == 4 ? 8 * kt + 2 * qq + w.hi : 4 * kt + qq;
         const bool use = w.row_ok[ct] && (PER == 4 || w.hi == 0) && mb != -INFINITY;
         const float e2 = exp2f((mb - M[ct]) * kKapLog2e);
