@@ -114,6 +114,18 @@ def test_kap_small(rt, case):
     check_kap(rt, name, inputs.generate(wl), stride, mode, budget)
 
 
+@pytest.mark.parametrize("stride,mode,budget", [(16, kap.MODE_FRACTION, 0.3), (8, kap.MODE_TOP_P, 0.9)])
+def test_kap_multi_chunk_sequences(rt, stride, mode, budget):
+    # a 19K-token sequence spans 38 (stride 16) or 76 (stride 8) key tiles of 32 samples:
+    # its query groups split their keys over two or three chunks whose row maxima combine
+    # in the workspace; the sequences around it put its tiles and the next sequence's at
+    # nonzero slots
+    lens = [64 * 9, 64 * 300 + 17, 64 * 40 + 5]
+    log("case multi-chunk", lens, "stride", stride, "mode", mode, "budget", budget)
+    wl = inputs.small_workload(f"chunks_s{stride}", lens, 4, 2, generator="structured", seed=91, pool="shuffled")
+    check_kap(rt, f"multi-chunk s{stride}", inputs.generate(wl), stride, mode, budget)
+
+
 def test_kap_rejects_unsupported(rt):
     import torch
     from block_sparse_long_osk_amd import binding
