@@ -67,19 +67,48 @@ __device__ __forceinline__ void radix_select(const uint32_t* hkey, int stride, i
   }
 }
 
-// Ascending bitonic sort of n (a power of two) keys in LDS by NT threads.
+// Ascending bitonic sort of n (a power of two) keys in LDS by NT threads.  The stages
+// of each merge size kk (partner distances kk/2, kk/4, .., 1) are taken up to three at
+// a time: the 2^t elements that t consecutive stages (distances 2^(p+t-1) .. 2^p) make
+// interact differ only in address bits p .. p+t-1, so one thread loads them, runs the t
+// stages' compare-exchanges in registers and stores them -- the same network, one LDS
+// round trip and one barrier per group of stages.
+template <int T>
+__device__ __forceinline__ void bitonic_stages(uint64_t* keys, int n, int kk, int p, int tid, int nt) {
+  constexpr int M = 1 << T;
+  for (int g = tid; g < (n >> T); g += nt) {
+    const int x0 = ((g >> p) << (p + T)) | (g & ((1 << p) - 1));
+    const bool up = (x0 & kk) == 0;  // bit kk lies above the group's bits: one direction
+    uint64_t e[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) e[m] = keys[x0 + (m << p)];
+#pragma unroll
+    for (int s = T - 1; s >= 0; --s) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (m & (1 << s)) continue;
+        const uint64_t u = e[m], v = e[m | (1 << s)];
+        if ((u > v) == up) {
+          e[m] = v;
+          e[m | (1 << s)] = u;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) keys[x0 + (m << p)] = e[m];
+  }
+}
 template <int NT>
 __device__ __forceinline__ void bitonic_block(uint64_t* keys, int n, int tid) {
   for (int kk = 2; kk <= n; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int x = tid; x < n; x += NT) {
-        const int y = x ^ jj;
-        if (y > x) {
-          const uint64_t p = keys[x], q = keys[y];
-          const bool up = (x & kk) == 0;
-          if ((p > q) == up) { keys[x] = q; keys[y] = p; }
-        }
-      }
+    int top = 0;  // log2 of the largest partner distance of this merge: kk / 2
+    while ((2 << top) < kk) ++top;
+    for (int hi = top; hi >= 0; hi -= 3) {
+      const int t = hi + 1 < 3 ? hi + 1 : 3;  // stages in this group: distances 2^hi .. 2^(hi-t+1)
+      const int p = hi - t + 1;
+      if (t == 3) bitonic_stages<3>(keys, n, kk, p, tid, NT);
+      else if (t == 2) bitonic_stages<2>(keys, n, kk, p, tid, NT);
+      else bitonic_stages<1>(keys, n, kk, p, tid, NT);
       __syncthreads();
     }
   }
