@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void mask_pool_kernel(const BuilderArgs a) {
   if (tid < kHeadDim) {
     float t = 0.f;
     for (int x = 0; x < 16; ++x) t += red[x][tid];
-    a.kbar[((int64_t)qb * a.hkv + g) * kHeadDim + tid] = has_page ? t / (float)rows : 0.f;
+    a.kbar[((int64_t)g * kHeadDim + tid) * a.total_qblocks + qb] = has_page ? t / (float)rows : 0.f;
   }
 }
 
@@ -178,20 +178,18 @@ __global__ __launch_bounds__(256) void mask_score_kernel(const BuilderArgs a) {
   __syncthreads();
   // block indices are clamped to the page-table width as in the select kernel
   const int jmax = min(i0 + ng - 1, a.max_pages - 1);
+  // kbar is stored dims-major ([hkv, 128, total_qblocks]): for each dim, consecutive
+  // threads read consecutive blocks' values
+  const float* kcol = a.kbar + (int64_t)g * kHeadDim * a.total_qblocks + qb0;
   for (int j = tid; j <= jmax; j += 256) {
-    const float* kb = a.kbar + ((int64_t)(qb0 + j) * a.hkv + g) * kHeadDim;
     float acc[kScoreGroup];
 #pragma unroll
     for (int q = 0; q < kScoreGroup; ++q) acc[q] = 0.f;
-    for (int d = 0; d < kHeadDim; d += 4) {
-      const float4 kv = *(const float4*)(kb + d);
+#pragma unroll 8
+    for (int d = 0; d < kHeadDim; ++d) {
+      const float kv = kcol[(int64_t)d * a.total_qblocks + j];
 #pragma unroll
-      for (int q = 0; q < kScoreGroup; ++q) {
-        acc[q] = fmaf(qs[q][d], kv.x, acc[q]);
-        acc[q] = fmaf(qs[q][d + 1], kv.y, acc[q]);
-        acc[q] = fmaf(qs[q][d + 2], kv.z, acc[q]);
-        acc[q] = fmaf(qs[q][d + 3], kv.w, acc[q]);
-      }
+      for (int q = 0; q < kScoreGroup; ++q) acc[q] = fmaf(qs[q][d], kv, acc[q]);
     }
 #pragma unroll
     for (int q = 0; q < kScoreGroup; ++q)

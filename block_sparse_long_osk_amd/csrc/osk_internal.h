@@ -56,7 +56,7 @@ struct BuilderArgs {
   int32_t* mask_len;
   float* scores;      // nullable (the caller's proxy_scores)
   float* qbar;        // workspace [total_qblocks, hkv, 128]
-  float* kbar;        // workspace [total_qblocks, hkv, 128]
+  float* kbar;        // workspace [hkv, 128, total_qblocks] (dims-major)
   float* score_rows;  // [total_qblocks, hkv, max_pages]: scores, or workspace when scores is null
   // per-q-head sets (union builder only; null otherwise)
   float* qbar_heads;       // workspace [total_qblocks, hq, 128]: each head's block mean
