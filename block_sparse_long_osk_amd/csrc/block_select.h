@@ -5,10 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "osk_internal.h"
+
 namespace cosa_osk {
 
+static_assert(kMaxPagesBuilder <= 65536, "radix_select skips the id word's upper digit passes");
+
 // Radix select: for each of nh segments (segment seg holds n keys whose 64-bit value is
-// (hkey[seg * stride + r] << 32) | (r + r0), all distinct), the k-th smallest key (k >= 1,
+// (hkey[seg * stride + r] << 32) | (r + r0), all distinct, r + r0 < 2^16), the k-th smallest key (k >= 1,
 // k <= n) into s_prefix[seg], by eight 8-bit digit passes that all segments share.  Waves
 // 0 .. nh-1 of the NT threads search the digit histograms.  Called by every thread; ends
 // with a barrier.
@@ -22,6 +26,9 @@ __device__ __forceinline__ void radix_select(const uint32_t* hkey, int stride, i
     s_k[tid] = k;
   }
   for (int pass = 0; pass < 8; ++pass) {
+    // the low word of a key is a block id below kMaxPagesBuilder <= 2^16: its digits at
+    // bits 16..31 are 0 for every key, so those passes would keep bin 0 and the count
+    if (pass == 4 || pass == 5) continue;
     const int shift = 56 - 8 * pass;
     const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
     for (int x = tid; x < nh * 256; x += NT) hist[x >> 8][x & 255] = 0;
