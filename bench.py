@@ -353,7 +353,7 @@ def main():
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "frac_of_attainable": tflops / attain["mfma_bf16_tflops"],
                 "kernel": ("osk_prefill_ring_kernel<4>" if B == 64 else "osk_prefill_b128_kernel<2>")
-                          + " (+ schedule kernel, 0.3% of the call)",
+                          + " (+ schedule kernel, 0.2% of the call)",
                 "algorithmic_flop_per_launch": flop,
                 "kv_gather_gbs": kv_bytes / (med * 1e-3) / 1e9,
                 "kv_gather_frac_of_hbm": kv_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}

@@ -296,19 +296,22 @@ __global__ __launch_bounds__(1024) void osk_schedule_kernel(const int32_t* __res
     base += x;
   }
   __syncthreads();
-  if (tid < 64) {  // stable scatter, 64 query blocks at a time, in index order
-    const int lane = tid;
+  {  // stable scatter: wave w fills the bins [w * per, (w + 1) * per) and walks every
+     // query block in index order, 64 at a time, so each bin is filled in index order
+    const int lane = tid & 63, wv = tid >> 6;
+    const int per = (nbins + 15) / 16;
+    const int lo = wv * per, hi = min(nbins, lo + per);
     for (int c0 = 0; c0 < n_qb; c0 += 64) {
       const int qb = c0 + lane;
-      const bool valid = qb < n_qb;
-      const int k = valid ? (int)key[qb] : -1;
-      uint64_t todo = __ballot(valid);
+      const int k = qb < n_qb ? (int)key[qb] : -1;
+      const bool mine = k >= lo && k < hi;
+      uint64_t todo = __ballot(mine);
       while (todo) {
         const int leader = __builtin_ctzll(todo);
         const int lk = __shfl(k, leader, 64);
-        const uint64_t same = __ballot(valid && k == lk);
+        const uint64_t same = __ballot(mine && k == lk);
         const int pos0 = hist[lk];
-        if (valid && k == lk) {
+        if (mine && k == lk) {
           const int rank = __popcll(same & ((1ull << lane) - 1ull));
           order[pos0 + rank] = qb;
         }
