@@ -370,8 +370,12 @@ __device__ __forceinline__ void load_q(const PrefillArgs& a, const Unit& u, int 
     if (row_ok) x = *(const i32x4_t*)(qrow + c * 16);
     qf[c] = __builtin_bit_cast(bf16x8_t, x);
   }
-  // Q must have landed before the visit loop: otherwise the compiler places its
-  // vmcnt wait inside the loop, where it would also drain the in-flight page gathers
+}
+// Q must have landed before the visit loop: otherwise the compiler places its vmcnt
+// wait inside the loop, where it would also drain the in-flight page gathers.  Called
+// after the window's visit list is resolved, so that Q's loads overlap the mask-row
+// and page-table loads.
+__device__ __forceinline__ void wait_q_landed() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
 }
 
@@ -716,6 +720,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
     const int nv = resolve_window<NT, SUB, kPage, HW>(a, u, mrow, k0, wl, wlds, wave, lane, u.h - hl);
+    wait_q_landed();
     // K tiles live in slots 0..3 of the first half of the ring, V tiles in the second
     // half; page p uses K slot p % 4 and V slot p % 4.
     auto k_slot = [&](int p) { return ring_addr + (uint32_t)(p % kRing) * kTileBytes; };
@@ -893,6 +898,7 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
     if (logging && quarter == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
     const int nv = resolve_window<NT, NPB, B, HW>(a, u, mrow, k0, wl, wlds, wave, lane, u.h - hl);
+    wait_q_landed();
     const int ntiles = 2 * nv;
     auto k_slot = [&](int t) { return ring_addr + (uint32_t)(t % kRing) * kTileBytes; };
     auto v_slot = [&](int t) { return ring_addr + (uint32_t)(kRing * kTileBytes) + (uint32_t)(t % kRing) * kTileBytes; };
