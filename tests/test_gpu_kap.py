@@ -103,6 +103,9 @@ SMALL = [
     ("mha_s16", [64 * 30 + 1], 2, 2, "iid", "shuffled", 16, kap.MODE_FRACTION, 0.2),
     ("gqa2_s8", [64 * 9, 64 * 9 + 63, 17], 4, 2, "structured", "shuffled", 8, kap.MODE_TOP_P, 0.8),
     ("gqa8_s16", [64 * 12 + 5], 16, 2, "structured", "identity", 16, kap.MODE_FRACTION, 0.25),
+    # an empty and a one-token sequence between ragged ones: no tiles, and one sampled key
+    ("edges_s16", [64 * 7 + 3, 0, 1, 64 * 5], 8, 2, "structured", "shuffled", 16, kap.MODE_FRACTION, 0.3),
+    ("edges_s8", [64 * 7 + 3, 0, 1, 64 * 5], 8, 2, "structured", "shuffled", 8, kap.MODE_TOP_P, 0.9),
 ]
 
 
