@@ -135,12 +135,23 @@ __global__ __launch_bounds__(64) void kap_pack_kernel(const KapArgs a, int per) 
     const int c = 32 * kt + m;
     ki32x4_t v = {0, 0, 0, 0};
     if (c < R) {
+      // a key is read only if its logical block is usable (every physical page
+      // holding one of the block's tokens is in the pool), as for the mean-pooled
+      // proxy and the prefill; otherwise the block has no stored keys and packs zero
       const int t = c * a.stride;
-      const int page = t / a.page_len;
-      const int ph = page < a.pt_stride ? pt[page] : -1;
-      if (ph >= 0 && ph < a.num_phys)
+      const int j = t / a.block, sub = a.block / a.page_len;
+      bool ok = true;
+      for (int x2 = 0; x2 < sub; ++x2) {
+        const int t0 = j * a.block + x2 * a.page_len;
+        const int e = j * sub + x2;
+        const int p = (t0 < L && e < a.pt_stride) ? pt[e] : (t0 < L ? -1 : 0);
+        ok = ok && p >= 0 && p < a.num_phys;
+      }
+      if (ok) {  // then t's own page entry was among those checked, inside the row
+        const int ph = pt[t / a.page_len];
         v = *(const ki32x4_t*)(a.k + (int64_t)ph * a.kv_sp + (int64_t)g * a.kv_sh +
                                 (int64_t)(t % a.page_len) * a.kv_st + gran * 8);
+      }
     }
     // dims 8 gran .. +8 = chunk gran / 2, lane half gran % 2
     *(ki32x4_t*)(dst + ((gran >> 1) * 64 + (gran & 1) * 32 + m) * 8) = v;

@@ -20,7 +20,9 @@ steps are taken in the pages' order:
 Readings of what the pages leave open (each is listed in the design notes):
 
 * Stride(X) keeps the first token of every group of s consecutive tokens of a
-  sequence: sample r is token r*s (r*s < L).  s divides the page size.
+  sequence: sample r is token r*s (r*s < L).  s divides the page size.  A sampled
+  key on a page whose page-table entry lies outside the physical pool has no
+  stored value and is taken as zero.
 * The causal mask acts on sampled positions: sample c is visible to sample r iff
   c <= r (token c*s <= token r*s).
 * d is the head dimension (scale 1/sqrt(d)).
@@ -57,8 +59,14 @@ def sampled_rows(L: int, stride: int) -> np.ndarray:
 def gather_sampled_keys(k_pool, pt_row, L: int, g: int, stride: int, page_size: int) -> np.ndarray:
     """K~ of one KV head: [R, d] float64, sample c being token c * stride."""
     toks = sampled_rows(L, stride)
-    pages = np.asarray(pt_row)[toks // page_size]
-    return np.asarray(k_pool[pages, g, toks % page_size, :], dtype=np.float64)
+    pt = np.asarray(pt_row, dtype=np.int64).reshape(-1)
+    idx = toks // page_size
+    pages = np.where(idx < pt.shape[0], pt[np.minimum(idx, max(pt.shape[0] - 1, 0))], -1)
+    stored = (pages >= 0) & (pages < k_pool.shape[0])
+    ks = np.zeros((toks.size, k_pool.shape[-1]))
+    # a sample on a page outside the pool has no stored key: it stays zero
+    ks[stored] = np.asarray(k_pool[pages[stored], g, toks[stored] % page_size, :], dtype=np.float64)
+    return ks
 
 
 def block_ranking(qs: np.ndarray, ks: np.ndarray, i: int, stride: int, page_size: int,

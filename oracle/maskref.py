@@ -12,7 +12,9 @@ readings taken here are:
 * qbar_{g,i} = sum over the q heads h of KV group g of the mean of q_h over the
   valid rows of query block i (grouped-query heads share one page set per KV
   head, as PageWeaver notes section 2 state);
-* kbar_{g,j} = mean of k_g over the tokens t < L of logical page j;
+* kbar_{g,j} = mean of k_g over the tokens t < L of logical page j; a page whose
+  page-table entry lies outside the physical pool has no stored keys and pools to
+  zero (it scores 0 and may be kept; the prefill then does not visit it);
 * score_{g,i,j} = qbar_{g,i} . kbar_{g,j} for causal pages j <= i;
 * forced pages F_i = {0, i} (either can be switched off); the rest R_i are the
   other causal pages; n_keep = ceil(b1 |R_i| - 1e-3) clamped to [0, |R_i|] (the
@@ -89,9 +91,11 @@ def pooled_proxies(q, k_pool, page_table, cu_seqlens, num_kv_heads: int, page_si
                 blk = np.asarray(q[a:b], dtype=np.float64)                 # [rows, Hq, d]
                 mean_h = blk.sum(axis=0) / (b - a)                         # [Hq, d]
                 qbar[i] = mean_h.reshape(num_kv_heads, G, d).sum(axis=1)
-                ph = int(page_table[s][i])
+                ph = int(page_table[s][i]) if i < len(page_table[s]) else -1
                 cnt = min(P, L - i * P)
-                kbar[i] = np.asarray(k_pool[ph, :, :cnt, :], dtype=np.float64).sum(axis=1) / cnt
+                if 0 <= ph < k_pool.shape[0]:
+                    kbar[i] = np.asarray(k_pool[ph, :, :cnt, :], dtype=np.float64).sum(axis=1) / cnt
+                # else: no stored keys, the pooled key stays zero (the block scores 0)
         out.append((qbar, kbar))
     return out
 

@@ -31,8 +31,9 @@ What it computes (sources are the pages this project follows):
   own pages in the union's order.
 
 Decision codes: 0 = computed, 1 = skipped in-kernel, 2 = not visited (mask
-padding, an id outside [0, n_pages), a non-causal id j > i, a repeated id, or an
-entry outside the head's membership).
+padding, an id outside [0, n_pages), a non-causal id j > i, a repeated id, a
+page whose page-table entry lies outside the physical pool, or an entry outside
+the head's membership).
 Margins are in natural-log units of the scaled logits; NaN where not visited.
 
 All arithmetic is float64 on the exact (bfloat16-valued) inputs.  The batched
@@ -78,17 +79,36 @@ def softmax_attention_row(q_row: np.ndarray, keys: np.ndarray, values: np.ndarra
 # ----------------------------------------------------------------------------
 # canonical visit list of one mask row
 # ----------------------------------------------------------------------------
-def canonical_visits(row: Sequence[int], length: int, block_index: int, n_pages: int) -> List[tuple]:
+def usable_pages(pt_row, n_pages: int, n_phys: int) -> np.ndarray:
+    """[n_pages] bool: logical page j of the sequence has a physical page in the pool.
+
+    PageWeaver notes, section 2.1 conventions: an id that does not name a stored
+    page adds no interaction.  A page-table entry outside [0, n_phys) (the -1 of an
+    unmapped page, or an id past the pool) therefore makes its logical page
+    unusable: a mask entry naming it is not visited.
+    """
+    pt = np.asarray(pt_row, dtype=np.int64).reshape(-1)
+    ok = np.zeros(max(n_pages, 0), dtype=bool)
+    w = min(n_pages, pt.shape[0])
+    ok[:w] = (pt[:w] >= 0) & (pt[:w] < n_phys)
+    return ok
+
+
+def canonical_visits(row: Sequence[int], length: int, block_index: int, n_pages: int,
+                     usable: Optional[np.ndarray] = None) -> List[tuple]:
     """(position k, logical page j) pairs that are visited, in mask order.
 
-    Entries past `length`, ids outside [0, n_pages), ids after the block (j > i)
-    and repeats of an id already visited are not visited.
+    Entries past `length`, ids outside [0, n_pages), ids after the block (j > i),
+    pages without a physical page in the pool (usable[j] false) and repeats of an
+    id already visited are not visited.
     """
     seen = set()
     out = []
     for k in range(min(int(length), len(row))):
         j = int(row[k])
         if j < 0 or j >= n_pages or j > block_index or j in seen:
+            continue
+        if usable is not None and not usable[j]:
             continue
         seen.add(j)
         out.append((k, j))
@@ -120,10 +140,14 @@ def brute_force_attention(q, k_pool, v_pool, page_table, cu_seqlens, order_mask,
     for s in range(S):
         t0, L = int(cu_seqlens[s]), int(cu_seqlens[s + 1] - cu_seqlens[s])
         n_pages = -(-L // page_size)
-        # keys/values of the sequence in logical token order
+        usable = usable_pages(page_table[s], n_pages, k_pool.shape[0])
+        # keys/values of the sequence in logical token order (zero on unusable pages,
+        # which no query can see)
         keys = np.zeros((L, Hkv, d))
         vals = np.zeros((L, Hkv, d))
         for j in range(n_pages):
+            if not usable[j]:
+                continue
             ph = int(page_table[s][j])
             n = min(page_size, L - j * page_size)
             keys[j * page_size: j * page_size + n] = np.asarray(k_pool[ph, :, :n, :], np.float64).transpose(1, 0, 2)
@@ -135,7 +159,8 @@ def brute_force_attention(q, k_pool, v_pool, page_table, cu_seqlens, order_mask,
                 if kept_pages is not None:
                     ids = kept_pages.get((qb, h), [])
                 else:
-                    ids = [j for _, j in canonical_visits(order_mask[qb, g], mask_len[qb, g], i, n_pages)]
+                    ids = [j for _, j in canonical_visits(order_mask[qb, g], mask_len[qb, g], i, n_pages,
+                                                          usable)]
                 for r in range(page_size):
                     c = i * page_size + r
                     if c >= L:
@@ -262,6 +287,8 @@ def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, h
     margins = np.full((nb, G, max_len), np.nan)
 
     rows_ = np.arange(nb)
+    usable = np.zeros(max(n_pages, 1), dtype=bool)
+    usable[:n_pages] = usable_pages(pt_row, n_pages, k_pool.shape[0])
     seen = np.zeros((nb, max(n_pages, 1)), dtype=bool)
     lens = np.asarray(mask_len[qbs, g], dtype=np.int64)
     ids_all = np.asarray(order_mask[qbs, g, :], dtype=np.int64)
@@ -270,6 +297,7 @@ def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, h
         ids = ids_all[:, k]
         visited = (k < lens) & (ids >= 0) & (ids < n_pages) & (ids <= blocks)
         jc = np.clip(ids, 0, max(n_pages - 1, 0))
+        visited &= usable[jc]
         visited &= ~seen[rows_, jc]
         if not visited.any():
             continue
@@ -278,19 +306,19 @@ def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, h
         j = jc[vb]
         phys = np.asarray(pt_row, dtype=np.int64)[j]
         Kp = np.asarray(k_pool[phys, g], dtype=np.float64)             # [n, P, d]
-        # line 12: S = Q K^T / sqrt(d); support: t < L and t <= c on this page
+        # scaled logits of this page (CoSA Eq. (1)); support t < L and t <= c (PageWeaver Eq. (1))
         Sv = sm_scale * np.matmul(Qb[vb], Kp[:, None, :, :].transpose(0, 1, 3, 2))  # [n, G, P, P]
         t_key = j[:, None] * P + key_off[None, :]                        # [n, P]
         c_row = rows[vb]                                                 # [n, P]
         vis = (t_key[:, None, :] < L) & (t_key[:, None, :] <= c_row[:, :, None]) & row_valid[vb][:, :, None]
         Sv = np.where(vis[:, None, :, :], Sv, -math.inf)
         m_loc = Sv.max(axis=3)                                           # [n, G, P]
-        # line 13: running max updated before the test
+        # running max updated before the skip test, whether or not the page is skipped
         m_old = m[vb]
         m_new = np.maximum(m_old, m_loc)
         diff = np.where(np.isneginf(m_loc), -math.inf, m_loc - np.where(np.isneginf(m_new), 0.0, m_new))
         margin = diff.max(axis=2)                                        # [n, G]
-        # line 14: skip iff Delta > 0 and max_r(m_loc - m) < ln(Delta / N)
+        # CoSA Eq. (5): skip iff Delta > 0 and max_r(m_loc - m) < ln(Delta / N)
         if tau is None:
             skip = np.zeros(margin.shape, dtype=bool)
         else:
@@ -307,7 +335,7 @@ def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, h
         m[vb] = np.where(mem[..., None], m_new, m_old)
         if not compute_output:
             continue
-        # lines 17-19 for the pages that are not skipped
+        # online softmax update of CoSA Eq. (2) for the pages that are not skipped
         comp = ~skip & mem                                               # [n, G]
         if not comp.any():
             continue
@@ -321,7 +349,7 @@ def _run_blocks(q, k_pool, v_pool, pt_row, t0, L, n_pages, qb_base, blocks, g, h
         lsum[vb] = np.where(cm, l_new, lsum[vb])
         o[vb] = np.where(cm[..., None], o_new, o[vb])
 
-    # line 21: O <- diag(l)^-1 O; zero output where nothing was accumulated
+    # final normalisation O / l; zero output where nothing was accumulated
     res = {"decisions": decisions, "margins": margins}
     pos = lsum > 0
     with np.errstate(divide="ignore"):

@@ -2,10 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see oracle/osk.py).
 
-Source: CoSA Appendix D.1 ("CoSA settings"): the logical key/value block size b and
-the physical KV-cache page size b_p are configured independently, and a logical
-block is resolved through one or more physical pages when b_p differs from b.  The
-pages give no more detail; the readings taken here are:
+Source: CoSA Appendix D.1 ("CoSA settings"): the attention block size b and the
+KV-cache page size b_p are two separate settings, so when they differ one logical
+block maps onto several stored pages (or part of one).  The section gives no more
+detail; the readings taken here are:
 
 * logical block j of a sequence holds its tokens b j .. b j + b - 1 (b = 64 or 128);
   token t is stored in physical page page_table[t // b_p] at row t % b_p (b_p

@@ -1,12 +1,15 @@
 """Parity of the KAP mask builder (cosa_build_kap_mask, through the C ABI) with the
 fp64 KAP oracle (CoSA section 4.2, Eq. (8)-(14)), on an MI355X.
 
-The kernel's block scores must match the oracle's within fp32 rounding; its HRM flags
-must match except where two blocks hold a row's maximum within fp32 rounding of the
-logits; every mask row must be exactly the order the kernel's own scores and flags
-define (HRM first, score descending, id ascending), with the fixed-fraction length
-exact and the Top-p length equal to the oracle's or off by one only where the
-cumulative score sits within rounding of the threshold.
+The kernel's block scores must match the oracle's to 1e-5 of max(1, |score|) (fp32
+logits and exponentials against fp64: the measured error is a few 1e-6); its HRM
+flags must match except where two blocks hold a row's maximum within fp32 rounding
+of the logits.  Every mask row is compared with the oracle's: it must be ordered by
+(HRM flag, oracle score) descending and hold the oracle's kept set, where two
+entries may trade places only if their fp64 scores are within that tolerance of
+each other (or a flag differs at a flag tie).  The fixed-fraction length is exact;
+the Top-p length equals the oracle's or is off by one only where the cumulative
+score sits within rounding of the threshold.
 """
 import math
 import sys
@@ -21,6 +24,7 @@ from tests.parity_helpers import oracle_arrays
 pytestmark = pytest.mark.gpu
 
 FLAG_TIE = 1e-4   # a Pbar within this of 1 may be the row maximum on either side
+SCORE_TOL = 1e-5  # block scores: |gpu - oracle| <= SCORE_TOL * max(1, |oracle|)
 
 
 def log(*a):
@@ -37,9 +41,30 @@ def rt():
     return runner
 
 
-def expected_row(s, h, n):
-    ids = np.arange(s.size)
-    return ids[np.lexsort((ids, -s.astype(np.float64), -h.astype(np.int64)))][:n]
+def check_row_against_oracle(row, so, flags, n_cand, tol):
+    """The GPU's mask row (its kept entries in visit order) against the oracle's scores
+    so and the flags the row is ranked by: in (flag desc, score desc) order up to tol,
+    and no left-out candidate ranked above a kept one by more than tol.  Returns
+    whether the row differs from the exact (flag, score, id) order."""
+    ids = np.arange(n_cand)
+    exact = ids[np.lexsort((ids, -so, -flags))][: row.size]
+    assert len(set(row.tolist())) == row.size and np.all((row >= 0) & (row < n_cand)), "row ids"
+    if np.array_equal(row, exact):
+        return False
+    fa, sa = flags[row], so[row]
+    for x in range(row.size - 1):
+        assert fa[x] > fa[x + 1] or (fa[x] == fa[x + 1] and sa[x] >= sa[x + 1] - tol), \
+            f"order at {x}: ({fa[x]}, {sa[x]}) before ({fa[x + 1]}, {sa[x + 1]})"
+    out = np.setdiff1d(ids, row)
+    if out.size and row.size:
+        # the weakest kept entry against the strongest left-out one
+        for f in (0, 1):
+            kept_f, out_f = sa[fa == f], so[out][flags[out] == f]
+            if out_f.size and kept_f.size:
+                assert kept_f.min() >= out_f.max() - tol, "kept set"
+        if (flags[out] == 1).any():
+            assert (fa == 1).all(), "a flagged candidate was left out while an unflagged one was kept"
+    return True
 
 
 def check_kap(rt, name, batch, stride, mode, budget, blocks=None, sm_scale=None):
@@ -57,15 +82,18 @@ def check_kap(rt, name, batch, stride, mode, budget, blocks=None, sm_scale=None)
                                                       page_size=B, width=om_g.shape[2], blocks=want,
                                                       return_hmax=True, sm_scale=sm_scale)
     starts = np.cumsum([0] + [-(-int(L) // B) for L in np.diff(batch.cu_seqlens)])
-    stats = dict(units=0, flag_ties=0, len_ties=0, max_score_err=0.0)
+    stats = dict(units=0, flag_ties=0, len_ties=0, rows_reordered=0, max_score_err=0.0, max_score_rel=0.0)
     for pos, qb in enumerate(want):
         sidx = int(np.searchsorted(starts, qb, side="right") - 1)
         i = qb - int(starts[sidx])
         for g in range(Hkv):
             stats["units"] += 1
             so, sg = sc_o[pos, g, : i + 1], sc_g[qb, g, : i + 1]
-            np.testing.assert_allclose(sg, so, rtol=2e-3, atol=2e-3, err_msg=f"{name} scores qb {qb} g {g}")
-            stats["max_score_err"] = max(stats["max_score_err"], float(np.max(np.abs(sg - so))))
+            scale = np.maximum(1.0, np.abs(so))
+            err = np.abs(sg.astype(np.float64) - so)
+            stats["max_score_err"] = max(stats["max_score_err"], float(err.max()))
+            stats["max_score_rel"] = max(stats["max_score_rel"], float((err / scale).max()))
+            assert np.all(err <= SCORE_TOL * scale), f"{name} scores qb {qb} g {g}: {float((err / scale).max())}"
             assert np.all(np.isnan(sc_g[qb, g, i + 1:])) and np.all(fl_g[qb, g, i + 1:] == 0)
             fo, fg = fl_o[pos, g, : i + 1].astype(bool), fl_g[qb, g, : i + 1].astype(bool)
             near = hm_o[pos, g, : i + 1] >= 1.0 - FLAG_TIE
@@ -77,11 +105,10 @@ def check_kap(rt, name, batch, stride, mode, budget, blocks=None, sm_scale=None)
             n = int(ml_g[qb, g])
             row = om_g[qb, g]
             assert np.all(row[n:] == -1)
-            assert list(row[:n]) == list(expected_row(sg, fg.astype(np.int64), n)), f"{name} order qb {qb} g {g}"
             if mode == kap.MODE_FRACTION:
                 assert n == int(ml_o[pos, g])
             elif n != int(ml_o[pos, g]):
-                order = expected_row(so, fo.astype(np.int64), i + 1)
+                order = np.lexsort((np.arange(i + 1), -so, -fo.astype(np.int64)))
                 cs = np.cumsum(so[order])
                 thr = np.float32(budget) * so.sum()
                 k = int(ml_o[pos, g])
@@ -89,6 +116,14 @@ def check_kap(rt, name, batch, stride, mode, budget, blocks=None, sm_scale=None)
                 edge = cs[min(n, k) - 1]
                 assert abs(edge - thr) <= 1e-3 * max(1.0, thr), f"{name} top-p edge qb {qb} g {g}"
                 stats["len_ties"] += 1
+            # the row against the oracle's scores, ranked by the flags the kernel took
+            # (equal to the oracle's except at the flag ties allowed above)
+            tol = SCORE_TOL * max(1.0, float(np.max(np.abs(so))))
+            try:
+                stats["rows_reordered"] += check_row_against_oracle(row[:n].astype(np.int64), so,
+                                                                    fg.astype(np.int64), i + 1, 2 * tol)
+            except AssertionError as e:
+                raise AssertionError(f"{name} row qb {qb} g {g}: {e}") from None
     assert stats["flag_ties"] <= max(2, stats["units"] // 100)
     log(name, stats)
     return stats

@@ -1,6 +1,6 @@
-"""Physical KV pages smaller than the logical block (CoSA Appendix D.1: a logical block
-is resolved through one or more physical pages when b_p differs from b), through the
-C ABI on an MI355X.
+"""Physical KV pages smaller than the logical block (CoSA Appendix D.1, "CoSA settings":
+the block size and the KV-cache page size are set independently, so one logical block
+may span several physical pages), through the C ABI on an MI355X.
 
 Paging is storage only, so with the same tokens re-paged at 16 or 32 tokens per
 physical page every result must be bitwise the one the 64-token layout gives: the

@@ -78,14 +78,23 @@ def test_unusable_physical_page_invalidates_its_block():
     pt_bad[0, 2 * 4 + 1] = -1                       # one of block 2's four physical pages
     kl, vl, ptl = paging.logical_view(kp, vp, pt_bad, cu, 16)
     assert ptl[0, 2] == -1 and np.all(ptl[0, [0, 1, 3]] >= 0)
-    # the prefill oracle then gives block 2's page no interaction, exactly as an invalid id
+    # the prefill oracle then gives block 2 no interaction: the result is that of the
+    # same rows with block 2 removed (a run that has no unusable page at all), and
+    # every entry naming block 2 is logged as not visited
     om = np.array([[[3, 2, 1, 0]]] * 4, dtype=np.int32).reshape(4, 1, 4)
     ml = np.full((4, 1), 4, dtype=np.int32)
-    a = osk.osk_reference(q, kl, vl, ptl, cu, om, ml, delta=-1.0)
-    pt64b = pt64.copy()
-    pt64b[0, 2] = -1
-    b = osk.osk_reference(q, k64, v64, pt64b, cu, om, ml, delta=-1.0)
-    np.testing.assert_array_equal(np.nan_to_num(np.asarray(a["out"]), nan=-3.0), np.nan_to_num(np.asarray(b["out"]), nan=-3.0))
+    om_rm = np.array([[[3, 1, 0, -1]]] * 4, dtype=np.int32).reshape(4, 1, 4)
+    ml_rm = np.full((4, 1), 3, dtype=np.int32)
+    delta = float(np.exp(-0.05) * lens[0])
+    a = osk.osk_reference(q, kl, vl, ptl, cu, om, ml, delta=delta)
+    b = osk.osk_reference(q, k64, v64, pt64, cu, om_rm, ml_rm, delta=delta)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["lse"], b["lse"], rtol=0, atol=1e-12)
+    rows_seeing_2 = [qb for qb in range(4) if qb >= 2]
+    for qb in rows_seeing_2:
+        assert np.all(a["decisions"][qb, :, 1] == osk.NOT_VISITED)
+        assert np.all(np.isnan(a["margins"][qb, :, 1]))
+        np.testing.assert_array_equal(a["decisions"][qb, :, [0, 2, 3]], b["decisions"][qb, :, [0, 1, 2]])
 
 
 def test_128_token_blocks_match_brute_force_and_repaging():
