@@ -12,7 +12,10 @@ dense causal mask and skipping off (the dense baseline), and the mask builder.
 Prints one JSON line.  value = effective TFLOP/s on the visited blocks:
 QK^T flops of every visited (q head, block) plus P V flops of the computed ones,
 each 2*b*b*128 for b-token logical blocks (b = 64, or 128 for the *_b128
-workload), over the median call time.
+workload), over the median call time.  The line's "configs" object holds the same
+measurements (median / p10 / p90 ms, effective TFLOP/s and its fraction of the
+bf16 peak, dense-mask speedup, skip ratio, builder time) for the other four
+workloads, taken in the same run.
 """
 import argparse
 import hashlib
@@ -36,7 +39,13 @@ TILE_FLOP = 2 * 64 * 64 * 128  # one 64x64x128 contraction
 def block_flop(block_size: int) -> float:
     """One b x b x 128 contraction (QK^T or P V of one visited (q head, block))."""
     return TILE_FLOP * (block_size // 64) ** 2
+
+
 KAP_STRIDE = 16
+# the five measured workloads; the one named by --workload is the headline, the
+# others go into the JSON line's "configs" object
+OTHER_WORKLOADS = ["cfg1_2k_mha", "cfg2_16k_gqa", "cfg3_32k_structured", "cfg4_128k_structured",
+                   "cfg5_paged_2seq"]
 KERNEL_SOURCES = ["block_sparse_long_osk_amd/csrc/osk_prefill.hip", "block_sparse_long_osk_amd/csrc/osk_internal.h"]
 # FETCH_SIZE / WRITE_SIZE summaries per workload (used while the kernel sources are unchanged)
 TRAFFIC_FILES = {
@@ -215,6 +224,10 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--workload", default="cfg4_128k_structured")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="measure the --workload only, not the other four workloads")
+    ap.add_argument("--other-steps", type=int, default=10,
+                    help="timed calls for each of the other workloads (3 warm-up calls each)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--mask", choices=["proxy", "kap", "union"], default="proxy",
                     help="skip-sweep: sweep with the mean-pooled proxy masks or with KAP masks (stride 16, "
@@ -261,6 +274,37 @@ def main():
             om, ml = runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1)
         skip_sweep(args, wl, db, om, ml, args.mask)
         return
+    rec = measure(args, wl, batch, db, om, ml, delta, headline=True)
+    # the other workloads, each measured the same way in this run (the headline's
+    # attainable rates, CPU baseline and KAP builder are not repeated)
+    if args.mask == "proxy" and not args.headline_only:
+        del db, om, ml
+        torch.cuda.empty_cache()
+        others = {}
+        for name in OTHER_WORKLOADS:
+            if name == wl.name:
+                continue
+            owl = inputs.WORKLOADS[name]
+            print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+            obatch = inputs.generate(owl)
+            odb = runner.upload(obatch)
+            oom, oml = runner.build_mask(odb, owl.budget1)
+            torch.cuda.synchronize()
+            others[name] = measure(args, owl, obatch, odb, oom, oml, inputs.skip_scale(name), headline=False)
+            del odb, oom, oml, obatch
+            torch.cuda.empty_cache()
+        rec["configs"] = others
+    print(json.dumps(rec), flush=True)
+
+
+def measure(args, wl, batch, db, om, ml, delta, headline):
+    """Times one workload: the prefill over its built mask (median, p10, p90 of
+    per-call HIP-event times), the dense-mask baseline and the mask builder; for the
+    headline also the KAP builder, the attainable rates, the roofline and the CPU
+    baseline.  Returns the record (the JSON line's body for the headline)."""
+    import torch
+    from block_sparse_long_osk_amd import binding, runner
+    steps, warmup = (args.steps, args.warmup) if headline else (args.other_steps, 3)
     # the timed prefill's mask: the mean-pooled proxy (default), KAP at the workload's budget
     # as the fixed fraction, or per-q-head sets as union rows with membership
     membership = None
@@ -280,8 +324,9 @@ def main():
         ws_b = torch.empty(binding.cosa_build_order_mask_workspace_bytes(db.dims(wb)), dtype=torch.uint8,
                            device="cuda")
         builder_ms, _ = time_calls(lambda: runner.build_mask(db, wl.budget1, workspace=ws_b), 5, 2)
+    del ws_b
     kap_ms = None
-    if db.num_q_heads // db.num_kv_heads * (db.block_size // KAP_STRIDE) <= 32:
+    if headline and db.num_q_heads // db.num_kv_heads * (db.block_size // KAP_STRIDE) <= 32:
         # the KAP builder (CoSA section 4.2): stride 16, fixed fraction = the workload's budget, and Top-p 0.95
         kw = binding.cosa_kap_mask_width(db.max_blocks, binding.COSA_KAP_TOP_P, 0.95)
         ws_k = torch.empty(binding.cosa_build_kap_mask_workspace_bytes(db.dims(kw)), dtype=torch.uint8, device="cuda")
@@ -298,7 +343,13 @@ def main():
     dec = logged.decisions
     visited = int((dec != 2).sum().item())
     computed = int((dec == 0).sum().item())
-    del logged, dec
+    # (query block, KV head, entry) visits where every q head of the group skips: their
+    # V tile is gathered but no head reads it
+    G = db.num_q_heads // db.num_kv_heads
+    d4 = dec.view(dec.shape[0], db.num_kv_heads, G, dec.shape[2])
+    kv_visits = int((d4 != 2).any(dim=2).sum().item())
+    all_skip = int((d4 == 1).all(dim=2).sum().item())
+    del logged, dec, d4
     B = db.block_size
     flop = block_flop(B) * (visited + computed)
 
@@ -307,14 +358,15 @@ def main():
     outs.lse = None
     ws = runner.workspace_for(db, width)
     step = lambda: runner.prefill(db, om, ml, delta, outputs=outs, workspace=ws, membership=membership)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    per, wall = time_calls(step, args.steps, args.warmup)
+    print(f"[bench] {wl.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    per, wall = time_calls(step, steps, warmup)
     med = statistics.median(per)
-    ms_per_step = wall / args.steps
+    ms_per_step = wall / steps
     aborts = runner.abort_count(db, ws, width)
     if aborts:
         print(f"[bench] {aborts} workgroups reported aborted inter-wave waits", file=sys.stderr)
     tflops = flop / (med * 1e-3) / 1e12
+    del outs, ws
 
     # ---- dense-mask baseline: same kernel, every causal page, skipping off
     dense = None
@@ -325,14 +377,32 @@ def main():
         douts = runner.allocate_outputs(db, dom.shape[2], log=False)
         douts.lse = None
         dws = runner.workspace_for(db, dom.shape[2])
-        print(f"[bench] timing dense baseline", file=sys.stderr, flush=True)
+        print(f"[bench] {wl.name}: timing dense baseline", file=sys.stderr, flush=True)
         dper, _ = time_calls(lambda: runner.prefill(db, dom, dml, -1.0, outputs=douts, workspace=dws),
                              args.dense_steps, 1)
         dmed = statistics.median(dper)
         dense = {"ms_per_layer": dmed, "tflops": d_flop / (dmed * 1e-3) / 1e12,
                  "frac_of_peak": d_flop / (dmed * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                  "visited_q_head_pages": d_visited, "algorithmic_tflop": d_flop / 1e12}
-        del douts, dom, dml
+        del douts, dom, dml, dws
+
+    kv_bytes = 2 * B * 128 * 2 * kv_visits
+    common = {
+        "ms_per_layer_median": med, "ms_p10": pct(per, 0.1), "ms_p90": pct(per, 0.9),
+        "effective_tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+        "visited_q_head_pages": visited, "computed_q_head_pages": computed,
+        "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
+        "all_heads_skip_fraction": all_skip / max(kv_visits, 1),
+        "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
+        "dense": dense, "mask_builder_ms": statistics.median(builder_ms),
+        "osk_plus_builder_ms": med + statistics.median(builder_ms),
+        "skip_scale_delta": delta, "aborted_workgroups": aborts,
+    }
+    if not headline:
+        common.update({"steps": steps, "warmup": warmup, "seq_lens": list(wl.seq_lens),
+                       "note": "latency-bound correctness case (32 workgroups): no roofline claim"
+                               if wl.num_q_heads == 1 else None})
+        return common
 
     # ---- attainable rates on this device (measurement-only kernels)
     print(f"[bench] calibrating MFMA and HBM rates", file=sys.stderr, flush=True)
@@ -348,15 +418,19 @@ def main():
             tr = json.load(f)
         if tr.get("workload") == wl.name and tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get("bytes_per_launch")
-    kv_bytes = 2 * B * 128 * 2 * (visited // (db.num_q_heads // db.num_kv_heads))
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "frac_of_attainable": tflops / attain["mfma_bf16_tflops"],
                 "kernel": ("osk_prefill_ring_kernel<4>" if B == 64 else "osk_prefill_b128_kernel<2>")
                           + " (+ schedule kernel, 0.2% of the call)",
                 "algorithmic_flop_per_launch": flop,
-                "kv_gather_gbs": kv_bytes / (med * 1e-3) / 1e9,
-                "kv_gather_frac_of_hbm": kv_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                # K and V tiles of every (query block, KV head) visit, as requested from the
+                # memory hierarchy (most are served by the L2s): not an HBM figure
+                "kv_gather_logical_gbs": kv_bytes / (med * 1e-3) / 1e9,
+                # bytes past the L2s (FETCH_SIZE + WRITE_SIZE, scaled; includes reads the
+                # last-level cache serves) per launch over the median launch time
+                "hbm_gbs_from_counters": (traffic / (med * 1e-3) / 1e9) if traffic else None,
+                "hbm_frac_from_counters": (traffic / (med * 1e-3) / 1e9 / PEAK_HBM_GBS) if traffic else None}
 
     cpu = None
     if not args.no_cpu:
@@ -364,26 +438,21 @@ def main():
         cpu = cpu_baseline(batch, wl, delta)
         cpu["ms_per_layer_extrapolated"] = flop / (cpu["value"] * 1e12) * 1e3
 
-    n_q_visits = visited
     rec = {
         "metric": "OSK prefill ms/layer + effective TFLOP/s at 128K; speedup vs dense-mask",
-        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step, "ms_per_layer_median": med, "ms_p10": pct(per, 0.1), "ms_p90": pct(per, 0.9),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
         "data": "synthetic (seeded structured generator; no dataset or model weights)",
         "config": {"workload": wl.name, "seq_len": wl.seq_lens[0] if len(wl.seq_lens) == 1 else list(wl.seq_lens),
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": 128,
                    "page_size": int(batch.k_pool.shape[2]), "block_size": B, "budget1": wl.budget1,
                    "skip_scale_delta": delta, "mask": args.mask},
-        "visited_q_head_pages": n_q_visits, "computed_q_head_pages": computed,
-        "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
-        "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
-        "dense": dense, "mask_builder_ms": statistics.median(builder_ms), "kap_builder": kap_ms,
-        "reuse_ratio": reuse,
-        "osk_plus_builder_ms": med + statistics.median(builder_ms),
-        "roofline": roofline, "attainable": attain, "cpu_baseline": cpu, "aborted_workgroups": aborts,
     }
-    print(json.dumps(rec), flush=True)
+    rec.update(common)
+    rec.update({"kap_builder": kap_ms, "reuse_ratio": reuse, "roofline": roofline, "attainable": attain,
+                "cpu_baseline": cpu})
+    return rec
 
 
 if __name__ == "__main__":

@@ -333,8 +333,7 @@ def repage(batch: Batch, page_size: int, seed: int) -> Batch:
 # ----------------------------------------------------------------------------
 # calibrated skip scales (written by the oracle's calibration script)
 # ----------------------------------------------------------------------------
-_DELTA_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                           "tests", "golden", "skip_scale_calibration.json")
+_DELTA_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "skip_scales.json")
 
 
 def skip_scale(name: str) -> float:

@@ -1,8 +1,8 @@
 """Freeze the skip scale Delta of each workload from the fp64 oracle's margins.
 
-TEST INFRASTRUCTURE (see oracle/osk.py).  Writes
-tests/golden/skip_scale_calibration.json; calls only oracle/ and the seeded
-input generator.  Usage:  python -m oracle.calibrate_skip_scale [names...]
+TEST INFRASTRUCTURE (see oracle/osk.py).  Writes the workload parameter table
+block_sparse_long_osk_amd/skip_scales.json (the package reads each workload's
+Delta from it); calls only oracle/ and the seeded input generator.  Usage:  python -m oracle.calibrate_skip_scale [names...]
 
 Why the margins suffice: Algorithm A of CoSA updates the running max before the
 skip test whether or not the page is skipped, so every visit's margin
@@ -33,7 +33,7 @@ import numpy as np
 from oracle import maskref, osk
 
 OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "tests", "golden", "skip_scale_calibration.json")
+                   "block_sparse_long_osk_amd", "skip_scales.json")
 TARGET_SKIP = 0.40
 IID_TAU = -1e-5
 

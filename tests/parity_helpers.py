@@ -14,7 +14,7 @@ import math
 import numpy as np
 
 from block_sparse_long_osk_amd import inputs
-from oracle import paging
+from oracle import decision_fixture, paging
 from oracle.osk import NOT_VISITED, ReplayDecisions, block_thresholds, osk_reference
 
 MAX_ABS = 1e-2
@@ -187,3 +187,35 @@ def check_mask_against_reference(gpu_om, gpu_ml, ref_om, ref_ml, ref_scores, rel
             # order: non-increasing scores up to the tolerance
             assert (np.diff(sa) <= tol).all(), (qb, g)
     return differ
+
+
+def check_full_decision_log(name, order_mask, mask_len, num_q_heads, gpu_decisions):
+    """Every visit's skip decision against the fp64 oracle's, stored for the full-size
+    workload by oracle/decision_fixture.py (CoSA section 3.3, Eq. (5)).
+
+    order_mask / mask_len: the oracle's mask the GPU ran (rebuilt by the test); the
+    stored per-row CRCs say which rows equal the ones the fixture was made from
+    (all of them unless the host's BLAS rounds a proxy score differently at a tie).
+    Decisions must be identical except where the oracle's margin is within 1e-3 of
+    the threshold; entries past a row's length must be logged as not visited."""
+    fx = decision_fixture.load(name)
+    nqb, hkv, width = order_mask.shape
+    G = num_q_heads // hkv
+    assert np.array_equal(np.asarray(mask_len, dtype=np.int32), fx["mask_len"]), "row lengths differ"
+    same_rows = decision_fixture.row_crcs(order_mask, mask_len) == fx["row_crc"]
+    visited = np.arange(width)[None, None, :] < np.repeat(mask_len, G, axis=1)[:, :, None]
+    assert visited.sum() == fx["n"]
+    gd = np.asarray(gpu_decisions)
+    assert gd.shape == (nqb, num_q_heads, width)
+    assert np.all(gd[~visited] == NOT_VISITED), "entries past the row length were visited"
+    g_vis = gd[visited]
+    assert np.all((g_vis == 0) | (g_vis == 1)), "a mask entry of a canonical row was not visited"
+    rows_ok = np.broadcast_to(np.repeat(same_rows, G, axis=1)[:, :, None], visited.shape)[visited]
+    differ = (g_vis == 1) != fx["skip"]
+    stats = dict(visits=int(fx["n"]), compared=int(rows_ok.sum()), rows_not_matching_fixture=int((~same_rows).sum()),
+                 skipped=int((g_vis == 1).sum()), near_ties=int((fx["near"] & rows_ok).sum()),
+                 near_tie_flips=int((differ & fx["near"] & rows_ok).sum()),
+                 disagreements=int((differ & ~fx["near"] & rows_ok).sum()))
+    assert stats["rows_not_matching_fixture"] <= max(1, same_rows.size // 1000), stats
+    assert stats["disagreements"] == 0, stats
+    return stats

@@ -18,8 +18,8 @@ import pytest
 
 from block_sparse_long_osk_amd import inputs
 from oracle import kap, maskref, osk
-from tests.parity_helpers import (check_mask_against_reference, check_prefill, delta_for_skip_fraction,
-                                  gpu_to_host, oracle_arrays)
+from tests.parity_helpers import (check_full_decision_log, check_mask_against_reference, check_prefill,
+                                  delta_for_skip_fraction, gpu_to_host, oracle_arrays)
 from tests.test_gpu_kap import check_kap
 
 pytestmark = pytest.mark.gpu
@@ -165,7 +165,7 @@ def test_b128_rejects_unsupported(rt):
 
 
 @pytest.mark.timeout(900)
-def test_b128_full_size_128k_sampled(rt):
+def test_b128_full_size_128k(rt):
     import torch
     name = "cfg4_128k_structured_b128"
     wl = inputs.WORKLOADS[name]
@@ -187,3 +187,5 @@ def test_b128_full_size_128k_sampled(rt):
     stats = check_prefill(bt, ref_om, ref_ml, delta, gpu, units)
     log(name, stats)
     assert stats["visited"] > 0
+    full = check_full_decision_log(name, ref_om, ref_ml, bt.q.shape[1], gpu["decisions"])
+    log(name, "full decision log:", full)

@@ -2,8 +2,9 @@
 
 Small shapes are compared in full (several tiles, ragged tails, packed sequences,
 shuffled page pools, every head-group layout); the five measured workloads run
-at full size in the launch configuration the benchmark times and are compared on
-sampled (query block, KV head) units, plus the whole decision log of those units.
+at full size in the launch configuration the benchmark times: the output of sampled
+(query block, KV head) units is compared with the oracle's, and every skip decision
+of the run with the oracle's decision log stored for that workload.
 """
 import math
 import os
@@ -16,8 +17,8 @@ from block_sparse_long_osk_amd import inputs
 from oracle import maskref
 from oracle.osk import full_causal_mask
 from tests.oracle_helpers import random_masks
-from tests.parity_helpers import (check_mask_against_reference, check_prefill, delta_for_skip_fraction,
-                                  gpu_to_host, host_arrays)
+from tests.parity_helpers import (check_full_decision_log, check_mask_against_reference, check_prefill,
+                                  delta_for_skip_fraction, gpu_to_host, host_arrays)
 
 pytestmark = pytest.mark.gpu
 
@@ -225,10 +226,14 @@ def test_cfg1_full(rt):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["cfg2_16k_gqa", "cfg3_32k_structured", "cfg4_128k_structured",
                                   "cfg5_paged_2seq"])
-def test_workload_sampled(rt, name):
-    """Full-size run in the benchmark's launch configuration; sampled units checked."""
+def test_workload_full_size(rt, name):
+    """Full-size run in the benchmark's launch configuration: the output of sampled
+    units against the oracle, and every skip decision of the run against the oracle's
+    stored decision log."""
     bt, om, ml, d = workload_case(name)
     units = sample_units(bt, 12, seed=len(name))
-    st, _ = run_and_check(rt, name, bt, om, ml, d, units=units)
+    st, gpu = run_and_check(rt, name, bt, om, ml, d, units=units)
     assert st["visited"] > 0
+    full = check_full_decision_log(name, om, ml, bt.q.shape[1], gpu["decisions"])
+    log(name, "full decision log:", full)
     _builder_parity(rt, name, bt, om, ml)
