@@ -61,6 +61,8 @@ def lib():
         L.cosa_osk_check_args.argtypes = [D, ctypes.c_size_t]
         L.cosa_osk_prefill.restype = ctypes.c_int
         L.cosa_osk_prefill.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t, P]
+        L.cosa_osk_prefill_noalloc.restype = ctypes.c_int
+        L.cosa_osk_prefill_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P]
         L.cosa_order_mask_width.restype = ctypes.c_int32
         L.cosa_order_mask_width.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_uint32]
         L.cosa_build_order_mask_workspace_bytes.restype = ctypes.c_size_t
@@ -95,7 +97,10 @@ EXPORTED = ["cosa_abi_version", "cosa_status_string", "cosa_osk_workspace_bytes"
             "cosa_osk_prefill", "cosa_order_mask_width", "cosa_build_order_mask_workspace_bytes",
             "cosa_build_order_mask", "cosa_validate_order_mask", "cosa_kap_mask_width",
             "cosa_build_kap_mask_workspace_bytes", "cosa_build_kap_mask", "cosa_osk_prefill_union",
-            "cosa_union_mask_width", "cosa_build_union_mask_workspace_bytes", "cosa_build_union_mask"]
+            "cosa_union_mask_width", "cosa_build_union_mask_workspace_bytes", "cosa_build_union_mask",
+            "cosa_osk_prefill_noalloc"]
+# bytes of the library-held scratch cosa_osk_prefill_noalloc uses (one copy per GPU)
+COSA_OSK_NOALLOC_SCRATCH_BYTES = 66048
 
 
 def _ptr(t) -> Optional[int]:
@@ -172,6 +177,16 @@ def cosa_osk_prefill(dims: CosaOskDims, q, k_pool, v_pool, page_table, cu_seqlen
                                 float(budget2), _ptr(out), _ptr(lse), _ptr(decisions), _ptr(margins),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "cosa_osk_prefill")
+
+
+def cosa_osk_prefill_noalloc(dims: CosaOskDims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask,
+                             mask_len, budget2: float, out, lse=None, decisions=None, margins=None, stream=None):
+    """The prefill with the library-held scratch in place of a workspace (allocates nothing)."""
+    st = lib().cosa_osk_prefill_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                                        _ptr(cu_seqlens), _ptr(cu_qblocks), _ptr(order_mask), _ptr(mask_len),
+                                        float(budget2), _ptr(out), _ptr(lse), _ptr(decisions), _ptr(margins),
+                                        _stream(stream))
+    _check(st, "cosa_osk_prefill_noalloc")
 
 
 def cosa_build_order_mask(dims: CosaOskDims, q, k_pool, page_table, cu_seqlens, cu_qblocks, budget1: float,

@@ -170,6 +170,22 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims, const void* q, const
                       budget2, out, lse, decisions, margins, workspace, workspace_bytes, stream);
 }
 
+cosa_status_t cosa_osk_prefill_noalloc(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* page_table, const int32_t* cu_seqlens,
+                                       const int32_t* cu_qblocks, const int32_t* order_mask,
+                                       const int32_t* mask_len, float budget2, void* out, float* lse,
+                                       uint8_t* decisions, float* margins, hipStream_t stream) {
+  const cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  static_assert(cosa_osk::kNoAllocScratchBytes == COSA_OSK_NOALLOC_SCRATCH_BYTES, "scratch size");
+  const size_t need = cosa_osk_workspace_bytes(dims);
+  if (need > cosa_osk::kNoAllocScratchBytes) return COSA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (cosa_osk::noalloc_scratch(&scratch) != hipSuccess) return COSA_ERR_HIP;
+  return prefill_impl(dims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len, nullptr,
+                      budget2, out, lse, decisions, margins, scratch, cosa_osk::kNoAllocScratchBytes, stream);
+}
+
 cosa_status_t cosa_osk_prefill_union(const cosa_osk_dims_t* dims, const void* q, const void* k_pool,
                                      const void* v_pool, const int32_t* page_table, const int32_t* cu_seqlens,
                                      const int32_t* cu_qblocks, const int32_t* order_mask, const int32_t* mask_len,

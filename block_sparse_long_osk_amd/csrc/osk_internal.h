@@ -126,6 +126,12 @@ __device__ __forceinline__ bool block_phys(const int32_t* pt_row, int n_pt, int 
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Bytes of the library-held prefill scratch (one copy per device): the prefill
+// workspace of kMaxQBlocks query blocks (schedule padded to 256 B, then the 256-byte
+// status block); and the address of the current device's copy (looked up on the
+// first call on each device).
+constexpr size_t kNoAllocScratchBytes = ((size_t)kMaxQBlocks * 4 + 1 + 255) / 256 * 256 + 256;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_build_kap_mask(const KapArgs& a, hipStream_t stream);
 hipError_t launch_build_order_mask(const BuilderArgs& a, hipStream_t stream);
 hipError_t launch_build_union_mask(const BuilderArgs& a, hipStream_t stream);

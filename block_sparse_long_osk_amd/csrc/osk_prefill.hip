@@ -47,6 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "osk_internal.h"
@@ -1000,6 +1001,36 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
   }
   if (logging && quarter == 0) fill_log_tail(a, u, lane);
   store_output<B>(a, u, o, l2, b2, r_blk, row_ok, lane);
+}
+
+// ---------------------------------------------------------------------------
+// library-held scratch for the prefill's workspace (callers that cannot allocate)
+// ---------------------------------------------------------------------------
+// The prefill's workspace (longest-first schedule and status block) for up to
+// kMaxQBlocks query blocks lives in this array, one copy per device, held until the
+// process ends.  Host code never uses the array's name as a device address: the
+// address of this device's copy is looked up once per device (with that device
+// current) and kept.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {

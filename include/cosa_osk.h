@@ -168,6 +168,33 @@ cosa_status_t cosa_osk_prefill(const cosa_osk_dims_t* dims,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * cosa_osk_prefill for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * kernels and results, with no workspace argument.  The workspace lives in a
+ * library-held device array of COSA_OSK_NOALLOC_SCRATCH_BYTES bytes, one copy per
+ * GPU, kept until the process ends; its address is looked up on the first call on
+ * each device (that call must run with the device current, as every call does).
+ * Limit: the workspace must fit the array (cosa_osk_workspace_bytes(dims) <=
+ * COSA_OSK_NOALLOC_SCRATCH_BYTES, which holds for every total_qblocks the library
+ * accepts); a larger need returns COSA_ERR_WORKSPACE before anything is launched.
+ * The call allocates nothing (no hipMalloc / hipFree, no allocating library call);
+ * each call rewrites the whole scratch it uses with kernels, so no state carries
+ * over between calls.  Every call on one GPU shares that GPU's array: calls that
+ * may overlap on one GPU (different streams, or different host threads without
+ * ordering) race and give undefined results -- order them on one stream.  The
+ * health word of cosa_osk_prefill stays in the scratch and is not reported.
+ * Arguments and errors otherwise as for cosa_osk_prefill.
+ */
+#define COSA_OSK_NOALLOC_SCRATCH_BYTES 66048
+cosa_status_t cosa_osk_prefill_noalloc(const cosa_osk_dims_t* dims,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* page_table, const int32_t* cu_seqlens,
+                                       const int32_t* cu_qblocks, const int32_t* order_mask,
+                                       const int32_t* mask_len, float budget2,
+                                       void* out, float* lse, uint8_t* decisions, float* margins,
+                                       hipStream_t stream);
+
+/*
  * The same prefill with a page set per q head (PageWeaver notes, section 2.2: the q
  * heads of a KV group traverse the union of their sets, and a membership mask keeps
  * each head's softmax to its own pages).  order_mask row (qb, g) is the union in
