@@ -69,10 +69,11 @@ def test_prefill_skips_unmapped_blocks_like_the_oracle(rt, case):
     log("case", case[0], "seq_lens", good.workload.seq_lens, "bad entries", case[6])
     q, k, _, pt_good, B = oracle_arrays(good)
     om, ml = maskref.build_order_mask(q, k, pt_good, good.cu_seqlens, good.k_pool.shape[1], 0.5, page_size=B)
-    # the oracle's logical view of the bad table has unusable blocks (-1 entries)
-    _, _, _, pt_bad_log, _ = oracle_arrays(bad)
-    unusable = sum(int((row[: -(-int(L) // B)] < 0).sum()) for row, L in zip(pt_bad_log, np.diff(bad.cu_seqlens)))
-    assert unusable >= len({(s, col * case[5] // B) for s, col, _ in case[6]})
+    # the blocks the oracle's view of the bad table cannot use (an entry outside its pool)
+    _, k_bad, _, pt_bad_log, _ = oracle_arrays(bad)
+    no_page = (pt_bad_log < 0) | (pt_bad_log >= k_bad.shape[0])
+    unusable = sum(int(row[: -(-int(L) // B)].sum()) for row, L in zip(no_page, np.diff(bad.cu_seqlens)))
+    assert unusable == len({(s, col * case[5] // B) for s, col, _ in case[6]})
     delta = delta_for_skip_fraction(bad, om, ml, 0.4)
     db = rt.upload(bad)
     omd, mld = rt.upload_mask(om, ml)
@@ -90,7 +91,7 @@ def test_prefill_skips_unmapped_blocks_like_the_oracle(rt, case):
         s = int(np.searchsorted(cu_qb, qb, side="right") - 1)
         for g in range(om.shape[1]):
             for kk in range(int(ml[qb, g])):
-                if pt_bad_log[s, om[qb, g, kk]] < 0:
+                if no_page[s, om[qb, g, kk]]:
                     n_bad_entries += 1
                     assert np.all(gpu["decisions"][qb, g * G:(g + 1) * G, kk] == 2)
     assert n_bad_entries > 0
