@@ -179,11 +179,13 @@ def cpu_baseline(batch, wl, delta, budget_s=15.0):
             "seconds": round(spent, 2)}
 
 
-def skip_sweep(args, wl, db, om, ml, mask_kind="proxy"):
+def skip_sweep(args, wl, db, om, ml, mask_kind="proxy", budget1=None):
     """Skip ratio and ms per call against Delta for two visit orders of the same page sets:
     the mask's own order (the mean-pooled proxy's score-descending order, or KAP's
     HRM-first order) and ascending page id.  tau = ln(Delta / L) is swept over a fixed
-    grid; the pages' own Delta = 2000 is included."""
+    grid; the pages' own Delta = 500, 2000 and 3000 are included.  Ends with the tau at
+    which each order reaches a 52 % skip ratio."""
+    rows = []
     import numpy as np
     import torch
     from block_sparse_long_osk_amd import runner
@@ -197,7 +199,10 @@ def skip_sweep(args, wl, db, om, ml, mask_kind="proxy"):
     orders = {mask_kind: (om, ml), "ascending": runner.upload_mask(asc, ml_h)}
     L = max(wl.seq_lens)
     deltas = [("tau", float(L * np.exp(t)), t) for t in (-1.0, -0.5, -0.3, -0.2, -0.15, -0.1, -0.05, -0.02, 0.0)]
-    deltas.append(("pages_delta", 2000.0, float(np.log(2000.0 / L))))
+    # the pages' own operating points (CoSA App. D.4: Delta = 500 with the remapped order,
+    # about 3000 without it, for a similar skip ratio; Delta = 2000 in the main results)
+    for d in (500.0, 2000.0, 3000.0):
+        deltas.append(("pages_delta", d, float(np.log(d / L))))
     outs = runner.allocate_outputs(db, width, log=False)
     outs.lse = None
     ws = runner.workspace_for(db, width)
@@ -213,7 +218,24 @@ def skip_sweep(args, wl, db, om, ml, mask_kind="proxy"):
             del logged, dec
             per, _ = time_calls(lambda: runner.prefill(db, m, mlen, delta, outputs=outs, workspace=ws), 5, 2)
             row[name] = {"skip_ratio": skipped / max(visited, 1), "ms_per_layer": statistics.median(per)}
+        row["budget1"] = budget1
+        rows.append(row)
         print(json.dumps(row), flush=True)
+    # tau at which each visit order reaches a 52 % skip ratio (linear interpolation over the
+    # tau grid), the pages' reference level for the remapped order
+    grid = sorted((r for r in rows if r["kind"] == "tau"), key=lambda r: r["tau_at_longest_seq"])
+    summary = {"mode": "skip-sweep-summary", "mask": mask_kind, "workload": wl.name, "budget1": budget1,
+               "target_skip": 0.52}
+    for name in orders:
+        hit = None
+        for r0, r1 in zip(grid, grid[1:]):
+            s0, s1 = r0[name]["skip_ratio"], r1[name]["skip_ratio"]
+            if s0 < 0.52 <= s1:
+                t0, t1 = r0["tau_at_longest_seq"], r1["tau_at_longest_seq"]
+                hit = t0 + (0.52 - s0) / (s1 - s0) * (t1 - t0)
+                break
+        summary[name] = None if hit is None else {"tau": hit, "delta": float(L * np.exp(hit))}
+    print(json.dumps(summary), flush=True)
 
 
 def main():
@@ -229,6 +251,8 @@ def main():
     ap.add_argument("--other-steps", type=int, default=10,
                     help="timed calls for each of the other workloads (3 warm-up calls each)")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--budget1", default=None,
+                    help="skip-sweep: comma-separated first-stage budgets to sweep (default: the workload's)")
     ap.add_argument("--mask", choices=["proxy", "kap", "union"], default="proxy",
                     help="skip-sweep: sweep with the mean-pooled proxy masks or with KAP masks (stride 16, "
                          "the workload's budget as the fixed fraction)")
@@ -270,9 +294,15 @@ def main():
                           "osk_calls": args.steps, "kernel_source_hash": kernel_source_hash()}))
         return
     if args.mode == "skip-sweep":
-        if args.mask == "kap":
-            om, ml = runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, wl.budget1)
-        skip_sweep(args, wl, db, om, ml, args.mask)
+        budgets = [float(x) for x in args.budget1.split(",")] if args.budget1 else [wl.budget1]
+        for b1 in budgets:
+            if args.mask == "kap":
+                om, ml = runner.build_kap_mask(db, KAP_STRIDE, binding.COSA_KAP_FRACTION, b1)
+            else:
+                om, ml = runner.build_mask(db, b1)
+            skip_sweep(args, wl, db, om, ml, args.mask, b1)
+            del om, ml
+            torch.cuda.empty_cache()
         return
     rec = measure(args, wl, batch, db, om, ml, delta, headline=True)
     # the other workloads, each measured the same way in this run (the headline's
