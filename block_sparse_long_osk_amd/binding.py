@@ -11,7 +11,10 @@ import math
 import os
 from typing import Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcosa_osk.so")
+# COSA_OSK_LIBRARY names another build of the same library (the host-sanitizer build
+# that the host-only ABI tests run against); by default the in-tree build is used
+LIB_PATH = os.environ.get("COSA_OSK_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libcosa_osk.so")
 
 COSA_OK = 0
 COSA_DECISION_COMPUTED, COSA_DECISION_SKIPPED, COSA_DECISION_NOT_VISITED = 0, 1, 2

@@ -1,6 +1,7 @@
 """Build libcosa_osk.so (HIP kernels for gfx950 + the C-ABI layer) in-tree with hipcc.
 
-    python -m block_sparse_long_osk_amd.build
+    python -m block_sparse_long_osk_amd.build               # the library (and the calibration one)
+    python -m block_sparse_long_osk_amd.build --host-asan   # host-sanitizer build under _build/asan
 """
 import os
 import shutil
@@ -33,15 +34,39 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
-def _link(sources, lib_path, verbose):
+# Host AddressSanitizer build of the attention library, for the host-only ABI tests
+# (argument checks and status codes; no kernel is launched from it).  The device code
+# is compiled as usual; only the host side is instrumented.
+ASAN_LIB_PATH = os.path.join(ROOT, "_build", "asan", "libcosa_osk.so")
+
+
+def asan_runtime() -> str:
+    """The compiler's ASan runtime, to be preloaded into the process that loads the
+    host-sanitizer build."""
+    base = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base), reverse=True) if os.path.isdir(base) else []:
+        cand = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    raise RuntimeError("the compiler's ASan runtime was not found")
+
+
+def build_host_asan(verbose: bool = False) -> str:
+    os.makedirs(os.path.dirname(ASAN_LIB_PATH), exist_ok=True)
+    _link(SOURCES, ASAN_LIB_PATH, verbose, opt="-O1",
+          extra=["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"])
+    return ASAN_LIB_PATH
+
+
+def _link(sources, lib_path, verbose, opt="-O3", extra=()):
     tmp = lib_path + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), "--offload-arch=gfx950", opt, "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms stay off in all device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # MFMA results in VGPRs: the softmax reads S with plain VALU ops and AGPRs
            # serve as spill space instead of holding S and O behind copy instructions
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
+           "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC] + list(extra)
     cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", tmp]
     if verbose:
@@ -57,4 +82,7 @@ def _link(sources, lib_path, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-asan" in sys.argv:
+        print(build_host_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
