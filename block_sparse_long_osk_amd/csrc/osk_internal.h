@@ -42,6 +42,7 @@ struct PrefillArgs {
   int32_t num_seqs, hq, hkv, total_qblocks, max_pages, num_phys, max_mask_len;
   int32_t pt_stride, page_len;  // page-table row length; tokens per physical page
   int32_t block;                // tokens per logical block (64 or 128)
+  int32_t heads_per_phase;      // KV heads the grid walks together (a divisor of hkv; set by the launcher)
   float sm_scale;
   float delta;
 };

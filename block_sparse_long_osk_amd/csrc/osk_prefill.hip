@@ -41,7 +41,9 @@
 // * a one-workgroup schedule kernel orders query blocks by mask length (longest
 //   first; stable), and the grid walks that order with the KV head minor, so
 //   consecutive workgroups (which the dispatcher spreads over the 8 XCDs round-
-//   robin) keep each KV head's pages in one XCD's L2.
+//   robin) keep each KV head's pages in one XCD's L2; the KV heads are taken in
+//   phases of as many heads as have their K and V pool slices fit in 192 MiB, so
+//   the pages in flight at any time stay within the 256 MB last-level cache.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -336,11 +338,19 @@ struct Unit {
 template <int HW, int B>
 __device__ __forceinline__ Unit decode_unit(const PrefillArgs& a, int heads_per_group, int nsub, int hl) {
   Unit u;
-  const int per_qb = a.hkv * nsub;
-  const int pos = blockIdx.x / per_qb;
-  const int rem = blockIdx.x - pos * per_qb;
-  u.g = rem / nsub;
-  const int sub = rem - u.g * nsub;
+  // The grid takes the KV heads in phases of heads_per_phase: every query block (in the
+  // longest-first order) for the first heads, then for the next ones.  Within a phase the
+  // KV head is minor, so consecutive workgroups, which the dispatcher deals out to the 8
+  // XCDs in turn, keep each KV head on the same XCDs.
+  const int hp = a.heads_per_phase;
+  const int per_phase = a.total_qblocks * hp * nsub;
+  const int phase = blockIdx.x / per_phase;
+  const int idx = blockIdx.x - phase * per_phase;
+  const int per_qb = hp * nsub;
+  const int pos = idx / per_qb;
+  const int rem = idx - pos * per_qb;
+  u.g = phase * hp + rem / nsub;
+  const int sub = rem - (rem / nsub) * nsub;
   u.qb = a.sched[pos];
   u.h = u.g * heads_per_group + sub * HW + hl;
   int lo = 0, hi_s = a.num_seqs;
@@ -1033,7 +1043,23 @@ hipError_t noalloc_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+// KV heads the grid works on together: the largest divisor of hkv whose pool slices (K
+// and V of every physical page of those heads) fit in kPhaseBytes, three quarters of the
+// chip's 256 MB last-level cache.  The pages that the concurrently running workgroups
+// gather then come from a working set that fits that cache, instead of from the whole
+// pool (537 MB at 128K tokens).
+constexpr int64_t kPhaseBytes = (int64_t)192 << 20;
+static int heads_per_phase(const PrefillArgs& a) {
+  const int64_t per_head = (int64_t)a.num_phys * a.page_len * kHeadDim * 2 * 2;
+  int best = 1;
+  for (int d = 1; d <= a.hkv; ++d)
+    if (a.hkv % d == 0 && (int64_t)d * per_head <= kPhaseBytes) best = d;
+  return best;
+}
+
+hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
+  PrefillArgs a = args;
+  a.heads_per_phase = heads_per_phase(a);
   if (a.total_qblocks == 0) return hipSuccess;
   const int G = a.hq / a.hkv;
   const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
