@@ -135,3 +135,29 @@ def test_full_size_128k_in_16_token_pages(rt):
         same = torch.equal(torch.nan_to_num(x.float(), nan=-9.0), torch.nan_to_num(y.float(), nan=-9.0))
         assert same, name
     log("cfg4 128K in 16-token pages: bitwise equal to 64-token pages")
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_pool_larger_than_a_phase(rt, block):
+    # The launcher takes the KV heads in phases whose K and V pool slices fit 192 MiB (a
+    # scheduling choice: it orders the units, nothing else).  A pool of 6,200 physical
+    # pages gives 203 MB per KV head, so the two KV heads here run one after the other;
+    # every result must be bitwise the one of the same tokens in a pool of their own
+    # pages (one phase), and match the fp64 oracle.
+    from tests.parity_helpers import oracle_arrays
+    wl = inputs.small_workload(f"phases{block}", [64 * 23 + 11, 64 * 8], 8, 2, generator="structured", seed=43,
+                               pool="shuffled")
+    small = inputs.generate(dataclasses.replace(wl, block_size=block))
+    big = inputs.generate(dataclasses.replace(wl, block_size=block, pool_pages=6200))
+    per_head = big.k_pool.shape[0] * big.k_pool.shape[2] * big.k_pool.shape[3] * 2 * 2
+    assert per_head > 192 << 20 > small.k_pool.shape[0] * 2 * per_head // big.k_pool.shape[0]
+    log("case", wl.name, "block", block, "phys pages", small.k_pool.shape[0], "vs", big.k_pool.shape[0])
+    q, k, _, pt, B = oracle_arrays(small)
+    om, ml = maskref.build_order_mask(q, k, pt, small.cu_seqlens, 2, 0.5, page_size=B)
+    delta = delta_for_skip_fraction(small, om, ml, 0.4)
+    a = run_prefill(rt, small, om, ml, delta)
+    b = run_prefill(rt, big, om, ml, delta)
+    assert_same(a, b, "phases")
+    stats = check_prefill(small, om, ml, delta, a)
+    log("one phase vs two: bitwise equal; oracle", stats)
+    assert stats["skipped"] > 0
