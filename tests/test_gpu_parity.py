@@ -84,6 +84,23 @@ def test_small_gqa_packed_paged(rt, hq, hkv):
     assert st["skipped"] > 0
 
 
+def test_many_short_sequences(rt):
+    # 48 packed sequences of random lengths (empty, one token, ragged tails, several
+    # blocks): each unit finds its sequence by a search over cu_qblocks, its causal
+    # range, its threshold ln(Delta / L_s) and its page-table row from its own entry.
+    rng = np.random.default_rng(23)
+    lens = [int(x) for x in rng.integers(0, 64 * 7, size=48)]
+    lens[3], lens[17], lens[30] = 0, 1, 64
+    wl = inputs.small_workload("many48", lens, 8, 2, generator="structured", seed=29, pool="shuffled")
+    bt = inputs.generate(wl)
+    log("case many48: lens", lens)
+    om, ml = oracle_mask(bt, 0.5)
+    run_and_check(rt, "many48/off", bt, om, ml, -1.0)
+    d = delta_for_skip_fraction(bt, om, ml, 0.4)
+    st, _ = run_and_check(rt, "many48/skip", bt, om, ml, d)
+    assert st["skipped"] > 0
+
+
 def test_empty_rows_junk_rows_and_all_skipped(rt):
     lens = [130, 70]
     wl = inputs.small_workload("edge", lens, 4, 1, generator="iid", seed=21)
