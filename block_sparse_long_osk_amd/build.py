@@ -1,8 +1,10 @@
 """Build libcosa_osk.so (HIP kernels for gfx950 + the C-ABI layer) in-tree with hipcc.
 
-    python -m block_sparse_long_osk_amd.build               # the library (and the calibration one)
+    python -m block_sparse_long_osk_amd.build               # the library, its checked variant, the calibration one
     python -m block_sparse_long_osk_amd.build --host-asan   # host-sanitizer build under _build/asan
+    python -m block_sparse_long_osk_amd.build --checked     # the bounds-checked library alone
 """
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -17,6 +19,12 @@ SOURCES = ["osk_prefill.hip", "mask_builder.hip", "kap.hip", "api.cpp"]
 # measurement-only microbenchmarks (attainable MFMA and HBM read rates), a library of their own
 CALIB_LIB_PATH = os.path.join(PKG, "libcosa_calib.so")
 CALIB_SOURCES = ["calib.hip"]
+# Bounds-checked variant of the attention library (same sources and ABI, built with
+# COSA_OSK_CHECKED): the prefill kernels test their index invariants -- schedule
+# positions, mask and page-table columns, physical page ids, output rows -- and count each
+# violation in the workspace health word.  Load it in place of the default library by
+# pointing COSA_OSK_LIBRARY at it.
+CHECKED_LIB_PATH = os.path.join(PKG, "libcosa_osk_checked.so")
 
 
 def hipcc() -> str:
@@ -27,10 +35,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link both shared libraries; returns the
+    """Compile every source for gfx950 and link the attention library, its bounds-checked
+    variant and the calibration library (three hipcc processes side by side); returns the
     attention library's path."""
-    _link(SOURCES, LIB_PATH, verbose)
-    _link(CALIB_SOURCES, CALIB_LIB_PATH, verbose)
+    jobs = [(SOURCES, LIB_PATH, {}), (SOURCES, CHECKED_LIB_PATH, {"extra": ["-DCOSA_OSK_CHECKED"]}),
+            (CALIB_SOURCES, CALIB_LIB_PATH, {})]
+    with concurrent.futures.ThreadPoolExecutor(len(jobs)) as pool:
+        futs = [pool.submit(_link, src, lib, verbose, **kw) for src, lib, kw in jobs]
+        for f in futs:
+            f.result()
     return LIB_PATH
 
 
@@ -56,6 +69,11 @@ def build_host_asan(verbose: bool = False) -> str:
     _link(SOURCES, ASAN_LIB_PATH, verbose, opt="-O1",
           extra=["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"])
     return ASAN_LIB_PATH
+
+
+def build_checked(verbose: bool = False) -> str:
+    _link(SOURCES, CHECKED_LIB_PATH, verbose, extra=["-DCOSA_OSK_CHECKED"])
+    return CHECKED_LIB_PATH
 
 
 def _link(sources, lib_path, verbose, opt="-O3", extra=()):
@@ -84,5 +102,7 @@ def _link(sources, lib_path, verbose, opt="-O3", extra=()):
 if __name__ == "__main__":
     if "--host-asan" in sys.argv:
         print(build_host_asan(verbose="-v" in sys.argv))
+    elif "--checked" in sys.argv:
+        print(build_checked(verbose="-v" in sys.argv))
     else:
         print(build(verbose="-v" in sys.argv))

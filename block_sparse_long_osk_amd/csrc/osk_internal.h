@@ -104,6 +104,21 @@ struct KapArgs {
   float budget, sm_scale;
 };
 
+// Checked build (compiled with COSA_OSK_CHECKED): the prefill kernels test the index
+// invariants they rely on -- schedule positions, mask columns, page-table columns, physical
+// page ids, output rows -- and count each violation in the workspace health word, which the
+// host reads back after the call (0 when healthy).  The default build compiles the tests away.
+#ifdef COSA_OSK_CHECKED
+#define COSA_CHECK(args, cond)                              \
+  do {                                                      \
+    if (!(cond)) atomicAdd((args).error_count, 1);          \
+  } while (0)
+#else
+#define COSA_CHECK(args, cond) \
+  do {                         \
+  } while (0)
+#endif
+
 // Physical pages of logical block j of a sequence (pt_row: its page-table row, n_pt
 // entries): the block is usable iff every page holding one of its tokens t < L is a
 // valid page id; then ph[0 .. block / page_len - 1] are set (pages past L repeat ph[0]).

@@ -351,8 +351,11 @@ __device__ __forceinline__ Unit decode_unit(const PrefillArgs& a, int heads_per_
   const int rem = idx - pos * per_qb;
   u.g = phase * hp + rem / nsub;
   const int sub = rem - (rem / nsub) * nsub;
+  COSA_CHECK(a, pos >= 0 && pos < a.total_qblocks && u.g < a.hkv);
   u.qb = a.sched[pos];
+  COSA_CHECK(a, u.qb >= 0 && u.qb < a.total_qblocks);
   u.h = u.g * heads_per_group + sub * HW + hl;
+  COSA_CHECK(a, u.h < a.hq);
   int lo = 0, hi_s = a.num_seqs;
   while (hi_s - lo > 1) {
     const int mid = (lo + hi_s) >> 1;
@@ -418,6 +421,7 @@ template <int NT, int NPB, int B, int HW>
 __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& u, const int32_t* mrow, int k0,
                                               int wl, WindowLds<NPB>& w, int wave, int lane, int h_first) {
   for (int e = threadIdx.x; e < wl; e += NT) {
+    COSA_CHECK(a, k0 + e < a.max_mask_len);
     const int id = mrow[k0 + e];
     int mbits = (1 << HW) - 1;
     if (a.membership != nullptr) {
@@ -430,6 +434,7 @@ __device__ __forceinline__ int resolve_window(const PrefillArgs& a, const Unit& 
     bool ok = false;
     if (id >= 0 && id < u.n_pages && id <= u.i) {
       if (NPB == 1) {
+        COSA_CHECK(a, id < a.pt_stride);
         ph[0] = u.pt_row[id];
         ok = ph[0] >= 0 && ph[0] < a.num_phys;
       } else {
@@ -607,6 +612,7 @@ __device__ __forceinline__ void maybe_rebase(float m2, float& b2, float& l2, f32
 // Decision and margin log of one head for mask entries k0 .. k0+wl-1.
 __device__ __forceinline__ void flush_log(const PrefillArgs& a, const Unit& u, int k0, int wl, const uint8_t* dec,
                                           const float* mar, int lane) {
+  COSA_CHECK(a, k0 >= 0 && k0 + wl <= a.max_mask_len);
   uint8_t* drow = a.decisions + ((int64_t)u.qb * a.hq + u.h) * a.max_mask_len + k0;
   float* mrw = a.margins ? a.margins + ((int64_t)u.qb * a.hq + u.h) * a.max_mask_len + k0 : nullptr;
   for (int x = lane; x < wl; x += 64) {
@@ -631,6 +637,7 @@ __device__ __forceinline__ void store_output(const PrefillArgs& a, const Unit& u
                                              float b2, int r_blk, bool row_ok, int lane) {
   const int hi = lane >> 5;
   const float inv_l = l2 > 0.f ? 1.f / l2 : 0.f;
+  COSA_CHECK(a, !row_ok || u.tok0 + u.i * B + r_blk < a.cu_seqlens[a.num_seqs]);
   uint16_t* orow = a.out + (int64_t)(u.tok0 + u.i * B + r_blk) * a.o_st + (int64_t)u.h * a.o_sh;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -731,6 +738,7 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
     if (logging && half == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
     const int nv = resolve_window<NT, SUB, kPage, HW>(a, u, mrow, k0, wl, wlds, wave, lane, u.h - hl);
+    COSA_CHECK(a, nv >= 0 && nv <= wl);
     wait_q_landed();
     // K tiles live in slots 0..3 of the first half of the ring, V tiles in the second
     // half; page p uses K slot p % 4 and V slot p % 4.
@@ -742,9 +750,11 @@ __global__ __launch_bounds__(128 * HW) void osk_prefill_ring_kernel(const Prefil
       const int jp = __builtin_amdgcn_readfirstlane(wlds.vis_j[p]) & 0xFFFF;
       const uint16_t* sub_base[SUB];
 #pragma unroll
-      for (int x = 0; x < SUB; ++x)
-        sub_base[x] = (is_v ? vbase : kbase) +
-                      (int64_t)__builtin_amdgcn_readfirstlane(wlds.vis_phys[p * SUB + x]) * a.kv_sp;
+      for (int x = 0; x < SUB; ++x) {
+        const int ph = __builtin_amdgcn_readfirstlane(wlds.vis_phys[p * SUB + x]);
+        COSA_CHECK(a, ph >= 0 && ph < a.num_phys);
+        sub_base[x] = (is_v ? vbase : kbase) + (int64_t)ph * a.kv_sp;
+      }
       tg.template issue<SUB>(sub_base, a.page_len, is_v ? v_slot(p) : k_slot(p), u.L - jp * kPage, is_v, wave,
                              lane);
     };
@@ -909,6 +919,7 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
     if (logging && quarter == 0)
       for (int x = lane; x < wl; x += 64) { dec_lds[hl][x] = 2; mar_lds[hl][x] = __builtin_nanf(""); }
     const int nv = resolve_window<NT, NPB, B, HW>(a, u, mrow, k0, wl, wlds, wave, lane, u.h - hl);
+    COSA_CHECK(a, nv >= 0 && nv <= wl);
     wait_q_landed();
     const int ntiles = 2 * nv;
     auto k_slot = [&](int t) { return ring_addr + (uint32_t)(t % kRing) * kTileBytes; };
@@ -925,6 +936,7 @@ __global__ __launch_bounds__(256 * HW) void osk_prefill_b128_kernel(const Prefil
 #pragma unroll
       for (int x = 0; x < SUB; ++x) {
         const int ph = __builtin_amdgcn_readfirstlane(wlds.vis_phys[blk * NPB + (NPB == 1 ? 0 : xs * SUB + x)]);
+        COSA_CHECK(a, ph >= 0 && ph < a.num_phys);
         sub_base[x] = (is_v ? vbase : kbase) + (int64_t)ph * a.kv_sp +
                       (NPB == 1 ? (int64_t)(xs * kPage) * a.kv_st : (int64_t)0);
       }

@@ -154,7 +154,11 @@ cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_
  *             word: the number of workgroups that could not complete their visits
  *             (nonzero would mean the output of those blocks is not valid).  The
  *             kernels synchronise their waves with workgroup barriers only, so it
- *             is 0 after every call; it is kept for callers that check it.
+ *             is 0 after every call; it is kept for callers that check it.  A
+ *             library built with COSA_OSK_CHECKED (libcosa_osk_checked.so) also
+ *             counts there every index invariant its prefill kernels find broken
+ *             (schedule position, mask or page-table column, physical page id,
+ *             output row); 0 means none was.
  * Numerics: fp32 accumulation of bf16 products for Q K^T, fp32 running max/sum,
  * probabilities rounded to bf16 for the P V product, fp32 output accumulator,
  * bf16 output.

@@ -45,6 +45,18 @@ def test_library_exports_every_declared_symbol():
     assert binding.cosa_status_string(-3).startswith("workspace")
 
 
+CHECKED_LIB_PATH = os.path.join(os.path.dirname(binding.LIB_PATH), "libcosa_osk_checked.so")
+
+
+@pytest.mark.skipif(not os.path.exists(CHECKED_LIB_PATH), reason="bounds-checked library not built")
+def test_checked_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(CHECKED_LIB_PATH)
+    for n in declared_functions(["cosa_osk.h"]):
+        assert hasattr(lib, n), n
+    lib.cosa_abi_version.restype = ctypes.c_int
+    assert lib.cosa_abi_version() == 2
+
+
 @pytest.mark.skipif(not os.path.exists(CALIB_LIB_PATH), reason="calibration library not built")
 def test_calibration_library_exports_and_host_checks():
     lib = ctypes.CDLL(CALIB_LIB_PATH)
