@@ -87,6 +87,43 @@ def time_calls(fn, steps, warmup):
     return per, wall
 
 
+def calib_mode():
+    """The MFMA calibration kernel with constant operands and with data-like random bf16 operands,
+    in short (4096-round, a few ms) and long (114,688-round, ~0.1 s) calls: rate and the clock it
+    implies at one 32x32x16 MFMA per 32 cycles on each of the 1024 SIMDs.  Under rocprofv3 --pmc
+    GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES show whether a difference is the clock or the
+    MFMA issue rate."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "block_sparse_long_osk_amd", "libcosa_calib.so"))
+    L.cosa_calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    L.cosa_calib_mfma_bf16.restype = ctypes.c_int32
+    L.cosa_calib_mfma_bf16_data.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                            ctypes.c_void_p]
+    L.cosa_calib_mfma_bf16_data.restype = ctypes.c_int32
+    L.cosa_calib_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.cosa_calib_mfma_bf16_flop.restype = ctypes.c_double
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nwg = 256 * 8
+    out = torch.empty(nwg * 4, dtype=torch.float32, device="cuda")
+    res = {"mode": "calib", "workgroups": nwg, "cases": []}
+    for kind, iters, warm in (("constant", 4096, 2), ("data", 4096, 2), ("constant", 4096 * 28, 3),
+                              ("data", 4096 * 28, 3)):
+        def f():
+            if kind == "constant":
+                rc = L.cosa_calib_mfma_bf16(ctypes.c_void_p(out.data_ptr()), nwg, iters, stream)
+            else:
+                rc = L.cosa_calib_mfma_bf16_data(ctypes.c_void_p(out.data_ptr()), nwg, iters, 12345, stream)
+            if rc != 0:
+                raise RuntimeError("calibration launch failed")
+        per, _ = time_calls(f, 5, warm)
+        tf = L.cosa_calib_mfma_bf16_flop(nwg, iters) / (statistics.median(per) * 1e-3) / 1e12
+        res["cases"].append({"operands": kind, "rounds": iters, "ms_median": statistics.median(per),
+                             "tflops": tf, "implied_clock_ghz": tf * 1e12 / (1024 * 1024) / 1e9})
+        print(f"[bench] calib {kind} {iters}: {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return res
+
+
 def calibrate():
     """Attainable bf16 MFMA rate (independent 32x32x16 MFMA chains on every SIMD) and
     HBM streaming-read rate (2 GiB, 16-byte loads) on this device, from the
@@ -112,6 +149,18 @@ def calibrate():
             raise RuntimeError("cosa_calib_mfma_bf16 failed")
     per, _ = time_calls(mfma, 5, 2)
     mfma_tflops = L.cosa_calib_mfma_bf16_flop(nwg, iters) / (statistics.median(per) * 1e-3) / 1e12
+    # sustained: data-like operands, ~100 ms per call after ~0.3 s of the same load, so the
+    # clock is the one power management settles on
+    L.cosa_calib_mfma_bf16_data.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                            ctypes.c_void_p]
+    L.cosa_calib_mfma_bf16_data.restype = ctypes.c_int32
+    long_iters = 4096 * 28
+
+    def mfma_data():
+        if L.cosa_calib_mfma_bf16_data(ctypes.c_void_p(out.data_ptr()), nwg, long_iters, 12345, stream) != 0:
+            raise RuntimeError("cosa_calib_mfma_bf16_data failed")
+    per, _ = time_calls(mfma_data, 5, 3)
+    sustained_tflops = L.cosa_calib_mfma_bf16_flop(nwg, long_iters) / (statistics.median(per) * 1e-3) / 1e12
     nbytes = 2 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     rwg = 256 * 16
@@ -125,8 +174,13 @@ def calibrate():
     read_gbs = nbytes / (statistics.median(per) * 1e-3) / 1e9
     del buf, rout, out
     return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_gbs": read_gbs,
-            "how": "independent v_mfma_f32_32x32x16_bf16 chains, 2048 workgroups x 4 waves; "
-                   "2 GiB streaming read with 16-byte loads (libcosa_calib.so)"}
+            "mfma_bf16_tflops_sustained": sustained_tflops,
+            # 1024 flop per clock per SIMD (one 32x32x16 MFMA per 32 cycles), 1024 SIMDs
+            "mfma_clock_ghz_sustained": sustained_tflops * 1e12 / (1024 * 1024) / 1e9,
+            "how": "independent v_mfma_f32_32x32x16_bf16 chains, 2048 workgroups x 4 waves (burst: 4096 "
+                   "rounds on constant operands; sustained: 114,688 rounds, ~0.1 s per call, on data-like "
+                   "random bf16 operands, after 3 such calls); 2 GiB streaming read with 16-byte loads "
+                   "(libcosa_calib.so)"}
 
 
 def pct(xs, p):
@@ -256,11 +310,13 @@ def main():
     ap.add_argument("--mask", choices=["proxy", "kap", "union"], default="proxy",
                     help="skip-sweep: sweep with the mean-pooled proxy masks or with KAP masks (stride 16, "
                          "the workload's budget as the fixed fraction)")
-    ap.add_argument("--mode", choices=["bench", "counters", "skip-sweep"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "counters", "skip-sweep", "calib"], default="bench",
                     help="counters: a plain 1 GiB device copy (the counter scale reference), then "
                          "--steps OSK calls; for rocprofv3 --pmc passes.  skip-sweep: in-kernel skip "
                          "ratio and time per call against Delta, with the proxy's visit order and with "
-                         "every mask row sorted ascending (one JSON line per Delta)")
+                         "every mask row sorted ascending (one JSON line per Delta).  calib: the MFMA "
+                         "calibration kernel on constant and on data-like operands, short and long "
+                         "calls (one JSON line; no workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the kernel shards by KV head or by "
@@ -269,6 +325,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.mode == "calib":
+        print(json.dumps(calib_mode()))
+        return
     from block_sparse_long_osk_amd import binding, inputs, runner
     binding.lib()
     wl = inputs.WORKLOADS[args.workload]
@@ -439,6 +498,7 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
     attain = calibrate()
     if dense:
         dense["frac_of_attainable"] = dense["tflops"] / attain["mfma_bf16_tflops"]
+        dense["frac_of_sustained_mfma"] = dense["tflops"] / attain["mfma_bf16_tflops_sustained"]
 
     # ---- roofline of the dominant kernel
     traffic = None
@@ -451,6 +511,7 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "frac_of_attainable": tflops / attain["mfma_bf16_tflops"],
+                "frac_of_sustained_mfma": tflops / attain["mfma_bf16_tflops_sustained"],
                 "kernel": ("osk_prefill_ring_kernel<4>" if B == 64 else "osk_prefill_b128_kernel<2>")
                           + " (+ schedule kernel, 0.2% of the call)",
                 "algorithmic_flop_per_launch": flop,

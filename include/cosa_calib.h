@@ -1,7 +1,7 @@
 /*
  * cosa_calib.h -- measurement-only microbenchmarks for MI355X (gfx950).
  *
- * Not part of the attention method: these two kernels measure the attainable
+ * Not part of the attention method: these kernels measure the attainable
  * bf16 MFMA rate and the attainable HBM streaming-read rate on the device at
  * hand, so that the prefill kernel's rate can be stated as a fraction of what the
  * chip delivers as well as of its published peaks.  Library: libcosa_calib.so.
@@ -33,7 +33,15 @@ extern "C" {
  * num_workgroups >= 1, iters >= 1. */
 int32_t cosa_calib_mfma_bf16(float* out, int32_t num_workgroups, int32_t iters, hipStream_t stream);
 
-/* Floating-point operations one cosa_calib_mfma_bf16 call performs (2 per multiply-add). */
+/* The same chains on data-like operands: bf16 values with random signs and mantissas and
+ * exponents over about 2^-8 .. 2^8 (a hash of seed, lane and element), two operand sets taken
+ * in turn, so the MFMA datapath toggles as on real data; for rates sustained over long runs,
+ * where power sets the clock.  `iters` counts rounds of 8 MFMAs as above and must be even
+ * (>= 2); the flop count is cosa_calib_mfma_bf16_flop(num_workgroups, iters). */
+int32_t cosa_calib_mfma_bf16_data(float* out, int32_t num_workgroups, int32_t iters, uint32_t seed,
+                                  hipStream_t stream);
+
+/* Floating-point operations one cosa_calib_mfma_bf16 (or _data) call performs (2 per multiply-add). */
 double cosa_calib_mfma_bf16_flop(int32_t num_workgroups, int32_t iters);
 
 /* Streaming read of `bytes` bytes at src (16-byte aligned, bytes a multiple of 16)

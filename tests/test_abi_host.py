@@ -61,7 +61,8 @@ def test_checked_library_exports_every_declared_symbol():
 def test_calibration_library_exports_and_host_checks():
     lib = ctypes.CDLL(CALIB_LIB_PATH)
     names = declared_functions(["cosa_calib.h"])
-    assert names == ["cosa_calib_mfma_bf16", "cosa_calib_mfma_bf16_flop", "cosa_calib_read"]
+    assert names == ["cosa_calib_mfma_bf16", "cosa_calib_mfma_bf16_data", "cosa_calib_mfma_bf16_flop",
+                     "cosa_calib_read"]
     for n in names:
         assert hasattr(lib, n), n
     lib.cosa_calib_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
@@ -74,6 +75,11 @@ def test_calibration_library_exports_and_host_checks():
                                     ctypes.c_void_p]
     assert lib.cosa_calib_mfma_bf16(None, 1, 1, None) == -1
     assert lib.cosa_calib_mfma_bf16(ctypes.c_void_p(16), 0, 1, None) == -1
+    lib.cosa_calib_mfma_bf16_data.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                              ctypes.c_void_p]
+    assert lib.cosa_calib_mfma_bf16_data(None, 1, 2, 7, None) == -1
+    assert lib.cosa_calib_mfma_bf16_data(ctypes.c_void_p(16), 0, 2, 7, None) == -1
+    assert lib.cosa_calib_mfma_bf16_data(ctypes.c_void_p(16), 1, 3, 7, None) == -1  # odd round count
     assert lib.cosa_calib_read(None, 16, ctypes.c_void_p(16), 1, None) == -1
     assert lib.cosa_calib_read(ctypes.c_void_p(16), 17, ctypes.c_void_p(16), 1, None) == -1
     assert lib.cosa_calib_read(ctypes.c_void_p(24), 16, ctypes.c_void_p(16), 1, None) == -1
