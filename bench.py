@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+OTHER_WARM_MS = 200.0          # minimum warm-up of each non-headline workload's timed calls
 TILE_FLOP = 2 * 64 * 64 * 128  # one 64x64x128 contraction
 
 
@@ -68,12 +69,19 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def time_calls(fn, steps, warmup):
+def time_calls(fn, steps, warmup, warm_ms=0.0):
     """Per-call durations (ms) from HIP events on the current stream, plus the
-    wall time of the whole timed region bracketed by synchronizations."""
+    wall time of the whole timed region bracketed by synchronizations.  Before the
+    timed calls: `warmup` untimed calls, and more until at least `warm_ms` of wall time
+    has gone by (the GPU clock needs some tens of ms of back-to-back load to settle)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
         fn()
+        n += 1
+        if warm_ms > 0 and n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -302,8 +310,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="measure the --workload only, not the other four workloads")
-    ap.add_argument("--other-steps", type=int, default=10,
-                    help="timed calls for each of the other workloads (3 warm-up calls each)")
+    ap.add_argument("--other-steps", type=int, default=20,
+                    help="timed calls for each of the other workloads (after at least 3 warm-up calls "
+                         "and %d ms of them)" % OTHER_WARM_MS)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--budget1", default=None,
                     help="skip-sweep: comma-separated first-stage budgets to sweep (default: the workload's)")
@@ -393,7 +402,10 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
     baseline.  Returns the record (the JSON line's body for the headline)."""
     import torch
     from block_sparse_long_osk_amd import binding, runner
+    # the headline takes exactly --warmup untimed calls; the other workloads, whose calls
+    # are short, are also warmed for OTHER_WARM_MS so their timed calls run at a settled clock
     steps, warmup = (args.steps, args.warmup) if headline else (args.other_steps, 3)
+    warm_ms = 0.0 if headline else OTHER_WARM_MS
     # the timed prefill's mask: the mean-pooled proxy (default), KAP at the workload's budget
     # as the fixed fraction, or per-q-head sets as union rows with membership
     membership = None
@@ -448,7 +460,7 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
     ws = runner.workspace_for(db, width)
     step = lambda: runner.prefill(db, om, ml, delta, outputs=outs, workspace=ws, membership=membership)
     print(f"[bench] {wl.name}: timing {steps} steps", file=sys.stderr, flush=True)
-    per, wall = time_calls(step, steps, warmup)
+    per, wall = time_calls(step, steps, warmup, warm_ms)
     med = statistics.median(per)
     ms_per_step = wall / steps
     aborts = runner.abort_count(db, ws, width)
@@ -468,7 +480,7 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
         dws = runner.workspace_for(db, dom.shape[2])
         print(f"[bench] {wl.name}: timing dense baseline", file=sys.stderr, flush=True)
         dper, _ = time_calls(lambda: runner.prefill(db, dom, dml, -1.0, outputs=douts, workspace=dws),
-                             args.dense_steps, 1)
+                             args.dense_steps, 1, warm_ms)
         dmed = statistics.median(dper)
         dense = {"ms_per_layer": dmed, "tflops": d_flop / (dmed * 1e-3) / 1e12,
                  "frac_of_peak": d_flop / (dmed * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
