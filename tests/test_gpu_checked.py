@@ -1,5 +1,6 @@
-"""The small-shape prefill parity tests again, against the bounds-checked build of the
-library (libcosa_osk_checked.so, built by build() with COSA_OSK_CHECKED), on an MI355X.
+"""The small-shape prefill parity tests and the largest-batch test again, against the
+bounds-checked build of the library (libcosa_osk_checked.so, built by build() with
+COSA_OSK_CHECKED), on an MI355X.
 
 In that build the prefill kernels test the index invariants they rely on -- schedule
 positions, order-mask and page-table columns, physical page ids, output rows -- and count
@@ -24,7 +25,8 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 FILES = ["test_gpu_parity.py", "test_gpu_edges.py", "test_gpu_paging.py", "test_gpu_union.py",
-         "test_gpu_block128.py", "test_gpu_unmapped_pages.py", "test_gpu_scale.py", "test_gpu_schedule.py"]
+         "test_gpu_block128.py", "test_gpu_unmapped_pages.py", "test_gpu_scale.py", "test_gpu_schedule.py",
+         "test_gpu_limits.py"]
 DESELECT = ("not full_size and not cfg1_full and not builder and not kap and not validator "
             "and not rejects")
 
@@ -72,5 +74,5 @@ def test_prefill_parity_under_the_checked_build(checked_env):
     with open(checked_env["COSA_OSK_HEALTH_CHECK"]) as f:
         calls = f.read().splitlines()
     log(f"{passed} tests passed, {len(calls)} prefill calls with a zero health word")
-    assert passed >= 40, tail
+    assert passed >= 43, tail
     assert len(calls) >= passed, "the health check did not run on every test"
