@@ -14,7 +14,7 @@
  * visiting, section 4.3).  It runs the tiled online softmax of section 3.1,
  * Eq. (1)-(2), and skips the value side of a visited page in-kernel when the
  * skip scale Delta > 0 and max_r(m_loc[r] - m[r]) < ln(Delta / N) (section 3.3,
- * Eq. (5); Algorithm A line 14), N being the sequence's valid length, the max
+ * Eq. (5); Algorithm A, the skip test), N being the sequence's valid length, the max
  * taken over the block's valid rows, and m updated before the test.  A query
  * at causal position c attends to the tokens of its visited, non-skipped pages
  * with t < L and t <= c (PageWeaver notes, section 2.1, Eq. (1)-(2)); an empty

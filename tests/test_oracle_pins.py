@@ -138,7 +138,7 @@ def test_order_invariance_without_skipping():
 
 
 def test_disable_switch():
-    """CoSA App. D.1 / Alg. A line 14: Delta = -1 and Delta = 0 both disable the skip."""
+    """CoSA App. D.1 and the skip test of Algorithm A: Delta = -1 and Delta = 0 both disable the skip."""
     rng = np.random.default_rng(12)
     q, k, v, pt, cu = make_problem(rng, [45], 2, 1, 8, 8, scale=2.0)
     om, ml = full_causal_mask(cu, 1, page_size=8)
