@@ -30,8 +30,8 @@
  * - The library keeps no state between calls; calls are thread-safe.  Calls
  *   that share a workspace must be ordered on one stream.
  * - Blocks and pages (CoSA Appendix D.1, "CoSA settings": the logical block size
- *   b and the physical KV-cache page size b_p are set independently, so one
- *   logical block may span several physical pages).  The logical block -- the query
+ *   the block size b and the page size b_p of the paged cache are two separate
+ *   settings, so one logical block may span several physical pages).  The logical block -- the query
  *   block, the mask's key block, the unit of a skip vote -- is b = block_size = 64
  *   or 128 tokens (Appendix D.1 uses 128: one vote per 128-row query tile).  The KV
  *   cache's physical pages hold b_p = page_size = 16, 32 or 64 tokens, or 128 when

@@ -1,6 +1,6 @@
-"""128-token logical blocks (CoSA Appendix D.1: logical query, key and value blocks of
-b = 128 tokens, one skip vote per 128-row query tile, each block resolved through the
-physical pages of the paged KV cache), through the C ABI on an MI355X.
+"""128-token logical blocks (CoSA Appendix D.1: b = 128 for queries, keys and values
+alike, one skip vote per 128-row query tile, each block found through the physical
+pages of the paged KV cache), through the C ABI on an MI355X.
 
 The prefill is checked against the fp64 oracle run at page size 128 on the logical
 view of the pool, for physical pages of 16, 32, 64 and 128 tokens, ragged tails that
