@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see oracle/osk.py).
 
 Source: CoSA Appendix D.1 ("CoSA settings"): the attention block size b and the
-KV-cache page size b_p are two separate settings, so when they differ one logical
+number of tokens b_p per stored page are two separate settings, so when they differ one logical
 block maps onto several stored pages (or part of one).  The section gives no more
 detail; the readings taken here are:
 
