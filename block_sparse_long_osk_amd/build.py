@@ -76,15 +76,29 @@ def build_checked(verbose: bool = False) -> str:
     return CHECKED_LIB_PATH
 
 
+# code-generation flags of every device compile
+DEVICE_FLAGS = [
+    "--offload-arch=gfx950", "-std=c++17",
+    # packed fp32 VALU forms stay off in all device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax reads S with plain VALU ops and AGPRs
+    # serve as spill space instead of holding S and O behind copy instructions
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+]
+
+
+def device_asm_cmd(source, out_path, defines=()):
+    """The hipcc command that writes the gfx950 assembly of one source file, compiled
+    exactly as in the library (for inspecting what a build contains)."""
+    return ([hipcc(), "-O3"] + DEVICE_FLAGS + ["--cuda-device-only", "-S", "-Wno-unused-result",
+                                               "-I", INCLUDE, "-I", CSRC]
+            + ["-D" + d for d in defines] + [os.path.join(CSRC, source), "-o", out_path])
+
+
 def _link(sources, lib_path, verbose, opt="-O3", extra=()):
     tmp = lib_path + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", opt, "-std=c++17", "-fPIC", "-shared",
-           # packed fp32 VALU forms stay off in all device code
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # MFMA results in VGPRs: the softmax reads S with plain VALU ops and AGPRs
-           # serve as spill space instead of holding S and O behind copy instructions
-           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC] + list(extra)
+    cmd = [hipcc(), opt] + DEVICE_FLAGS + ["-fPIC", "-shared", "-Wno-unused-result", "-I", INCLUDE,
+                                           "-I", CSRC] + list(extra)
     cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", tmp]
     if verbose:
