@@ -1,10 +1,15 @@
-"""The prefill at the largest batch the library accepts -- 16,384 query blocks, the
-schedule kernel's and the no-allocation scratch's limit -- through the C ABI on an MI355X.
+"""The prefill at the largest inputs the library accepts, through the C ABI on an MI355X.
 
-1,024 packed sequences of 961..1,024 tokens (16 query blocks each, ragged tails) with
-two q heads on one KV head, a shuffled page pool and random ordered masks with junk
-entries; skipping on.  Checked: the longest-first schedule (read back from the
-workspace) against a stable sort on the host; cosa_osk_prefill_noalloc bitwise against
+* 16,384 query blocks (the schedule kernel's and the no-allocation scratch's limit): 1,024
+  packed sequences of 961..1,024 tokens (16 query blocks each, ragged tails) with two q
+  heads on one KV head, a shuffled page pool and random ordered masks with junk entries.
+* 16,384 logical blocks in one sequence (the limit of the visited-page bitmap): one
+  sequence of 1,048,576 - 37 tokens, one head, rows of ids drawn over the whole causal
+  range (repeats included, so the first-occurrence rule is exercised in every word of
+  the bitmap).
+
+Skipping on in both.  Checked: the longest-first schedule (read back from the workspace)
+against a stable sort on the host; cosa_osk_prefill_noalloc bitwise against
 cosa_osk_prefill on every output; and sampled (query block, KV head) units against the
 fp64 oracle (output, LSE, decisions and margins), with the skip scale chosen from the
 oracle's margins on those units.
@@ -59,21 +64,45 @@ def delta_from_units(batch, om, ml, units, fraction=0.4):
     return float(math.exp(0.5 * (x[kq - 1] + x[kq])))
 
 
-def test_largest_batch_schedule_noalloc_and_oracle(rt):
+def spread_rows(rng, n_blocks, width):
+    """One sequence's rows: the diagonal block first, then width - 1 ids drawn uniformly
+    (with repeats) from the causal blocks 0 .. i."""
+    om = np.full((n_blocks, 1, width), -1, dtype=np.int64)
+    ml = np.zeros((n_blocks, 1), dtype=np.int64)
+    for i in range(n_blocks):
+        om[i, 0, 0] = i
+        om[i, 0, 1:] = rng.integers(0, i + 1, size=width - 1)
+        ml[i, 0] = width
+    return om, ml
+
+
+def _case(name, rng):
+    if name == "qblocks":
+        lens = rng.integers(961, 1025, size=NUM_SEQS)
+        wl = inputs.small_workload("limits", lens.tolist(), 2, 1, generator="iid", seed=91, pool="shuffled")
+        bt = inputs.generate(wl)
+        om, ml = random_masks(rng, lens.tolist(), 1, 64, WIDTH, junk=True, full_fraction=0.6)
+        extra = {0, 1, 15, 16, bt.total_qblocks - 16, bt.total_qblocks - 1}
+    else:
+        wl = inputs.small_workload("limits_seq", [16384 * 64 - 37], 1, 1, generator="structured", seed=93,
+                                   pool="shuffled")
+        bt = inputs.generate(wl)
+        om, ml = spread_rows(rng, bt.total_qblocks, WIDTH)
+        extra = {0, 1, 2, 8191, 8192, 16382, 16383}
+    picks = sorted(set(rng.choice(bt.total_qblocks, size=40, replace=False).tolist()) | extra)
+    return bt, om, ml, [(qb, 0) for qb in picks]
+
+
+@pytest.mark.parametrize("name", ["qblocks", "blocks_per_sequence"])
+def test_largest_inputs_schedule_noalloc_and_oracle(rt, name):
     import torch
     from block_sparse_long_osk_amd import binding
     rng = np.random.default_rng(3)
-    lens = rng.integers(961, 1025, size=NUM_SEQS)
-    wl = inputs.small_workload("limits", lens.tolist(), 2, 1, generator="iid", seed=91, pool="shuffled")
-    bt = inputs.generate(wl)
+    bt, om, ml, units = _case(name, rng)
     assert bt.total_qblocks == 16384
-    om, ml = random_masks(rng, lens.tolist(), 1, 64, WIDTH, junk=True, full_fraction=0.6)
-    picks = sorted(set(rng.choice(bt.total_qblocks, size=40, replace=False).tolist()) |
-                   {0, 1, 15, 16, bt.total_qblocks - 16, bt.total_qblocks - 1})
-    units = [(qb, 0) for qb in picks]
     delta = delta_from_units(bt, om, ml, units)
-    log("query blocks", bt.total_qblocks, "tokens", int(bt.cu_seqlens[-1]), "width", WIDTH, "delta", delta,
-        "sampled units", len(units))
+    log(name, "query blocks", bt.total_qblocks, "sequences", bt.num_seqs, "tokens", int(bt.cu_seqlens[-1]),
+        "width", WIDTH, "delta", delta, "sampled units", len(units))
 
     db = rt.upload(bt)
     omd, mld = rt.upload_mask(om, ml)
