@@ -453,6 +453,8 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
     del logged, dec, d4
     B = db.block_size
     flop = block_flop(B) * (visited + computed)
+    nb = [-(-L // B) for L in db.seq_lens]
+    causal = sum(n * (n + 1) // 2 for n in nb) * db.num_q_heads  # (q head, block) pairs j <= i
 
     # ---- timed OSK calls (no logging)
     outs = runner.allocate_outputs(db, width, log=False)
@@ -493,6 +495,9 @@ def measure(args, wl, batch, db, om, ml, delta, headline):
         "effective_tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
         "visited_q_head_pages": visited, "computed_q_head_pages": computed,
         "skip_ratio": 1.0 - computed / max(visited, 1), "algorithmic_tflop": flop / 1e12,
+        # against every causal (q head, block) pair: the first stage's realized budget and the
+        # share left after both stages
+        "realized_stage1_budget": visited / max(causal, 1), "computed_fraction": computed / max(causal, 1),
         "all_heads_skip_fraction": all_skip / max(kv_visits, 1),
         "speedup_vs_dense": (dense["ms_per_layer"] / med) if dense else None,
         "dense": dense, "mask_builder_ms": statistics.median(builder_ms),
