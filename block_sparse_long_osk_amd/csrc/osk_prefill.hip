@@ -41,9 +41,10 @@
 // * a one-workgroup schedule kernel orders query blocks by mask length (longest
 //   first; stable), and the grid walks that order with the KV head minor, so
 //   consecutive workgroups (which the dispatcher spreads over the 8 XCDs round-
-//   robin) keep each KV head's pages in one XCD's L2; the KV heads are taken in
-//   phases of as many heads as have their K and V pool slices fit in 192 MiB, so
-//   the pages in flight at any time stay within the 256 MB last-level cache.
+//   robin) keep each KV head's pages on the same XCDs' L2s (8 / heads_per_phase
+//   XCDs per head); the KV heads are taken in phases of as many heads as have
+//   their K and V pool slices fit in 192 MiB, so the pages in flight at any time
+//   stay within the 256 MB last-level cache.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
