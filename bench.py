@@ -329,7 +329,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the kernel shards by KV head or by "
-              "query-block range without exchange inside a layer, but multi-GPU runs are not part of this build",
+              "query-block range without exchange inside a layer, but this library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
