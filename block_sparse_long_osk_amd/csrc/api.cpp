@@ -32,8 +32,10 @@ int32_t max_blocks(const cosa_osk_dims_t* d) {
 cosa_status_t check_dims(const cosa_osk_dims_t* d) {
   if (d == nullptr) return COSA_ERR_INVALID_ARG;
   if (d->block_size != 0 && d->block_size != 64 && d->block_size != 128) return COSA_ERR_UNSUPPORTED;
+  // an empty batch (no query blocks) may come with a page table of no columns
   if (d->num_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->total_q_tokens < 0 ||
-      d->total_qblocks < 0 || d->max_pages_per_seq < 1 || d->num_phys_pages < 0 || d->max_mask_len < 0)
+      d->total_qblocks < 0 || d->max_pages_per_seq < (d->total_qblocks > 0 ? 1 : 0) || d->num_phys_pages < 0 ||
+      d->max_mask_len < 0)
     return COSA_ERR_INVALID_ARG;
   if (d->head_dim != kHeadDim) return COSA_ERR_UNSUPPORTED;
   // physical pages of 16, 32 or 64 tokens, or 128 under 128-token blocks: a page
@@ -48,9 +50,13 @@ cosa_status_t check_dims(const cosa_osk_dims_t* d) {
   // every query block holds 1..block tokens
   if ((int64_t)d->total_q_tokens > (int64_t)blk * d->total_qblocks || d->total_qblocks > d->total_q_tokens)
     return COSA_ERR_INVALID_ARG;
-  if (!stride_ok(d->q_stride_tok) || !stride_ok(d->q_stride_head) || !stride_ok(d->o_stride_tok) ||
-      !stride_ok(d->o_stride_head) || !stride_ok(d->kv_stride_page) || !stride_ok(d->kv_stride_head) ||
-      !stride_ok(d->kv_stride_tok))
+  // the strides of an empty Q / output (no tokens) or an empty pool (no pages) are never
+  // used; array libraries give such tensors arbitrary (often zero) strides
+  if (d->total_q_tokens > 0 && (!stride_ok(d->q_stride_tok) || !stride_ok(d->q_stride_head) ||
+                                !stride_ok(d->o_stride_tok) || !stride_ok(d->o_stride_head)))
+    return COSA_ERR_INVALID_ARG;
+  if (d->num_phys_pages > 0 &&
+      (!stride_ok(d->kv_stride_page) || !stride_ok(d->kv_stride_head) || !stride_ok(d->kv_stride_tok)))
     return COSA_ERR_INVALID_ARG;
   if (isnan(d->sm_scale) || isinf(d->sm_scale)) return COSA_ERR_INVALID_ARG;
   // page gathers address a page's tokens with 32-bit byte offsets
@@ -111,7 +117,14 @@ static cosa_status_t prefill_impl(const cosa_osk_dims_t* dims, const void* q, co
                                   const uint8_t* membership, float budget2, void* out, float* lse,
                                   uint8_t* decisions, float* margins, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-  cosa_status_t st = cosa_osk_check_args(dims, workspace_bytes);
+  cosa_status_t st = check_dims(dims);
+  if (st != COSA_OK) return st;
+  if (dims->total_qblocks == 0) {
+    // an empty batch reads and writes nothing: its pointers and workspace are not checked
+    if (isnan(budget2) || (margins != nullptr && decisions == nullptr)) return COSA_ERR_INVALID_ARG;
+    return COSA_OK;
+  }
+  st = cosa_osk_check_args(dims, workspace_bytes);
   if (st != COSA_OK) return st;
   if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr ||
       cu_qblocks == nullptr || mask_len == nullptr || out == nullptr ||
@@ -180,6 +193,9 @@ cosa_status_t cosa_osk_prefill_noalloc(const cosa_osk_dims_t* dims, const void* 
   static_assert(cosa_osk::kNoAllocScratchBytes == COSA_OSK_NOALLOC_SCRATCH_BYTES, "scratch size");
   const size_t need = cosa_osk_workspace_bytes(dims);
   if (need > cosa_osk::kNoAllocScratchBytes) return COSA_ERR_WORKSPACE;
+  if (dims->total_qblocks == 0)  // nothing to launch: the scratch is not looked up
+    return prefill_impl(dims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len, nullptr,
+                        budget2, out, lse, decisions, margins, nullptr, 0, stream);
   void* scratch = nullptr;
   if (cosa_osk::noalloc_scratch(&scratch) != hipSuccess) return COSA_ERR_HIP;
   return prefill_impl(dims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len, nullptr,
@@ -192,7 +208,8 @@ cosa_status_t cosa_osk_prefill_union(const cosa_osk_dims_t* dims, const void* q,
                                      const uint8_t* membership, float budget2, void* out, float* lse,
                                      uint8_t* decisions, float* margins, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
-  if (membership == nullptr && dims != nullptr && dims->max_mask_len > 0) return COSA_ERR_INVALID_ARG;
+  if (membership == nullptr && dims != nullptr && dims->max_mask_len > 0 && dims->total_qblocks > 0)
+    return COSA_ERR_INVALID_ARG;
   return prefill_impl(dims, q, k_pool, v_pool, page_table, cu_seqlens, cu_qblocks, order_mask, mask_len,
                       membership, budget2, out, lse, decisions, margins, workspace, workspace_bytes, stream);
 }
@@ -233,12 +250,14 @@ cosa_status_t cosa_build_order_mask(const cosa_osk_dims_t* dims, const void* q, 
   cosa_status_t st = check_dims(dims);
   if (st != COSA_OK) return st;
   if (max_blocks(dims) > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
-  if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
-      order_mask == nullptr || mask_len == nullptr)
+  const bool empty = dims->total_qblocks == 0;  // reads and writes nothing: pointers unchecked
+  if (!empty && (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr ||
+                 cu_qblocks == nullptr || order_mask == nullptr || mask_len == nullptr))
     return COSA_ERR_INVALID_ARG;
   if (!(budget1 >= 0.f && budget1 <= 1.f)) return COSA_ERR_INVALID_ARG;
   if ((flags & ~(uint32_t)(COSA_FORCE_FIRST | COSA_FORCE_DIAG)) != 0u) return COSA_ERR_INVALID_ARG;
   if (dims->max_mask_len < cosa_order_mask_width(max_blocks(dims), budget1, flags)) return COSA_ERR_INVALID_ARG;
+  if (empty) return COSA_OK;
   const size_t need = cosa_build_order_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
   cosa_osk::BuilderArgs a{};
@@ -313,12 +332,15 @@ cosa_status_t cosa_build_union_mask(const cosa_osk_dims_t* dims, const void* q, 
   if (max_blocks(dims) > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
   const int32_t G = dims->num_q_heads / dims->num_kv_heads;
   if (G > 32) return COSA_ERR_UNSUPPORTED;  // a candidate's head bits are one 32-bit word
-  if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
-      order_mask == nullptr || mask_len == nullptr || membership == nullptr || head_len == nullptr)
+  const bool empty = dims->total_qblocks == 0;  // reads and writes nothing: pointers unchecked
+  if (!empty && (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr ||
+                 cu_qblocks == nullptr || order_mask == nullptr || mask_len == nullptr || membership == nullptr ||
+                 head_len == nullptr))
     return COSA_ERR_INVALID_ARG;
   if (!(budget1 >= 0.f && budget1 <= 1.f)) return COSA_ERR_INVALID_ARG;
   if ((flags & ~(uint32_t)(COSA_FORCE_FIRST | COSA_FORCE_DIAG)) != 0u) return COSA_ERR_INVALID_ARG;
   if (dims->max_mask_len < cosa_union_mask_width(max_blocks(dims), G, budget1, flags)) return COSA_ERR_INVALID_ARG;
+  if (empty) return COSA_OK;
   const size_t need = cosa_build_union_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
@@ -404,8 +426,9 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   cosa_status_t st = check_dims(dims);
   if (st != COSA_OK) return st;
   if (max_blocks(dims) > cosa_osk::kMaxPagesBuilder) return COSA_ERR_UNSUPPORTED;
-  if (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr || cu_qblocks == nullptr ||
-      order_mask == nullptr || mask_len == nullptr)
+  const bool empty = dims->total_qblocks == 0;  // reads and writes nothing: pointers unchecked
+  if (!empty && (q == nullptr || k_pool == nullptr || page_table == nullptr || cu_seqlens == nullptr ||
+                 cu_qblocks == nullptr || order_mask == nullptr || mask_len == nullptr))
     return COSA_ERR_INVALID_ARG;
   if (mode != COSA_KAP_FRACTION && mode != COSA_KAP_TOP_P) return COSA_ERR_INVALID_ARG;
   if (mode == COSA_KAP_FRACTION ? !(budget > 0.f && budget <= 1.f) : !(budget >= 0.f && budget <= 1.f))
@@ -420,6 +443,7 @@ cosa_status_t cosa_build_kap_mask(const cosa_osk_dims_t* dims, const void* q, co
   const int rb = G * (blk / stride);
   if (rb > 32 || (rb & (rb - 1)) != 0) return COSA_ERR_UNSUPPORTED;
   if (dims->max_mask_len < cosa_kap_mask_width(max_blocks(dims), mode, budget)) return COSA_ERR_INVALID_ARG;
+  if (empty) return COSA_OK;
   const size_t need = cosa_build_kap_mask_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return COSA_ERR_WORKSPACE;
   cosa_osk::KapArgs a{};

@@ -29,9 +29,14 @@
  *   a launch failure is reported as COSA_ERR_HIP.
  * - The library keeps no state between calls; calls are thread-safe.  Calls
  *   that share a workspace must be ordered on one stream.
- * - Blocks and pages (CoSA Appendix D.1, "CoSA settings": the logical block size
- *   the block size b and the page size b_p of the paged cache are two separate
- *   settings, so one logical block may span several physical pages).  The logical block -- the query
+ * - An empty batch (total_qblocks == 0: every sequence has length 0) reads and
+ *   writes nothing: the prefill and builder calls check dims and their scalar
+ *   arguments, launch nothing and return COSA_OK; their pointers may then be NULL
+ *   and no workspace is needed.  cosa_validate_order_mask still zeroes its
+ *   counters.
+ * - Blocks and pages (CoSA Appendix D.1, "CoSA settings": the block size b and
+ *   the page size b_p of the paged cache are two separate settings, so one
+ *   logical block may span several physical pages).  The logical block -- the query
  *   block, the mask's key block, the unit of a skip vote -- is b = block_size = 64
  *   or 128 tokens (Appendix D.1 uses 128: one vote per 128-row query tile).  The KV
  *   cache's physical pages hold b_p = page_size = 16, 32 or 64 tokens, or 128 when
@@ -49,7 +54,9 @@
  *   kv_stride_tok <= 2^24 elements (a page's byte offsets fit in 32 bits).
  *   Anything else returns COSA_ERR_UNSUPPORTED.
  * - Layouts (element strides; head_dim is contiguous; strides are multiples of
- *   8 elements and the base pointers are 16-byte aligned):
+ *   8 elements and the base pointers are 16-byte aligned; the strides of q and out
+ *   are not checked when total_q_tokens is 0, those of the pools when
+ *   num_phys_pages is 0):
  *     q, out        [total_q_tokens, num_q_heads, 128]   (sequences packed on T)
  *     k_pool,v_pool [num_phys_pages, num_kv_heads, page_size, 128] (same strides)
  *     page_table    int32 [num_seqs, max_pages_per_seq]   page-sized token range -> physical page
@@ -100,7 +107,7 @@ typedef struct cosa_osk_dims {
   int32_t page_size;          /* tokens per physical KV page: 16, 32, 64 (128 if block_size is 128) */
   int32_t total_q_tokens;     /* T = cu_seqlens[num_seqs] */
   int32_t total_qblocks;      /* cu_qblocks[num_seqs] */
-  int32_t max_pages_per_seq;  /* row stride of page_table (physical pages per sequence) */
+  int32_t max_pages_per_seq;  /* row stride of page_table (physical pages per sequence); >= 1, or 0 in an empty batch */
   int32_t num_phys_pages;     /* pool size; a physical id outside [0, n) is not visited */
   int32_t max_mask_len;       /* row stride of order_mask and of the decision log */
   float sm_scale;             /* logit scale; <= 0 selects 1/sqrt(head_dim) */
@@ -158,7 +165,8 @@ cosa_status_t cosa_osk_check_args(const cosa_osk_dims_t* dims, size_t workspace_
  *             library built with COSA_OSK_CHECKED (libcosa_osk_checked.so) also
  *             counts there every index invariant its prefill kernels find broken
  *             (schedule position, mask or page-table column, physical page id,
- *             output row); 0 means none was.
+ *             output row); 0 means none was.  A call on an empty batch launches
+ *             nothing and leaves the workspace, health word included, untouched.
  * Numerics: fp32 accumulation of bf16 products for Q K^T, fp32 running max/sum,
  * probabilities rounded to bf16 for the P V product, fp32 output accumulator,
  * bf16 output.

@@ -32,6 +32,8 @@ def _health_checked_prefill(monkeypatch):
         if kw.get("workspace") is None:
             kw["workspace"] = runner.workspace_for(db, width)
         outs = plain(db, order_mask, mask_len, delta, *args, **kw)
+        if db.total_qblocks == 0:  # nothing launched: the workspace is not written
+            return outs
         torch.cuda.synchronize()
         bad = runner.abort_count(db, kw["workspace"], width)
         assert bad == 0, f"the checked kernels counted {bad} index-invariant violations"

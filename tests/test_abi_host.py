@@ -243,3 +243,46 @@ def test_union_entry_points_reject_bad_arguments_before_launch():
     assert call(dd=good_dims(max_mask_len=width - 1)) == INVALID          # narrower than the union can be
     assert call(wsb=need - 1) == WORKSPACE
     assert call(dd=good_dims(num_q_heads=40 * 8, max_mask_len=64 * 40)) == UNSUPPORTED   # 40 heads per group
+
+
+def test_empty_batch_needs_no_pointers_or_workspace():
+    """total_qblocks = 0 (every sequence empty): the prefill and builder entry points check
+    dims and their scalar arguments, launch nothing and return OK with NULL pointers and
+    no workspace (nothing is read or written); scalar errors are still reported."""
+    L = binding.lib()
+    d = good_dims(num_seqs=2, total_q_tokens=0, total_qblocks=0, max_mask_len=64)
+    nul = [None] * 8
+    assert L.cosa_osk_prefill(ctypes.byref(d), *nul, 1.0, None, None, None, None, None, 0, None) == OK
+    assert L.cosa_osk_prefill_noalloc(ctypes.byref(d), *nul, 1.0, None, None, None, None, None) == OK
+    assert L.cosa_osk_prefill_union(ctypes.byref(d), *nul, None, 1.0, None, None, None, None, None, 0,
+                                    None) == OK
+    assert L.cosa_osk_prefill(ctypes.byref(d), *nul, float("nan"), None, None, None, None, None, 0,
+                              None) == INVALID
+    assert L.cosa_osk_prefill(ctypes.byref(d), *nul, 1.0, None, None, None, 0x10000, None, 0, None) == INVALID
+    def build(b1=0.1):
+        return L.cosa_build_order_mask(ctypes.byref(d), None, None, None, None, None, b1, 3, None, None, None,
+                                       None, 0, None)
+    assert build() == OK
+    assert build(b1=1.5) == INVALID
+    assert L.cosa_build_union_mask(ctypes.byref(d), None, None, None, None, None, 0.1, 3, None, None, None, None,
+                                   None, 0, None) == OK
+    def kap(stride=16):
+        return L.cosa_build_kap_mask(ctypes.byref(d), None, None, None, None, None, stride, 0, 0.1, None, None,
+                                     None, None, None, 0, None)
+    assert kap() == OK
+    assert kap(stride=12) == UNSUPPORTED
+    # the strides of an empty Q / output and of an empty pool are not checked (zero-element
+    # arrays often carry zero strides); a non-empty one still needs valid strides
+    dz = good_dims(num_seqs=2, total_q_tokens=0, total_qblocks=0, q_stride_tok=0, q_stride_head=0,
+                   o_stride_tok=0, o_stride_head=0, max_mask_len=64)
+    assert L.cosa_osk_prefill(ctypes.byref(dz), *nul, 1.0, None, None, None, None, None, 0, None) == OK
+    assert binding.cosa_osk_check_args(good_dims(q_stride_tok=0), 1 << 20) == INVALID
+    assert binding.cosa_osk_check_args(good_dims(num_phys_pages=0, kv_stride_page=0, kv_stride_head=0,
+                                                 kv_stride_tok=0), 1 << 20) == OK
+    assert binding.cosa_osk_check_args(good_dims(kv_stride_tok=0), 1 << 20) == INVALID
+    # a page table of no columns is accepted for an empty batch only
+    d0 = good_dims(num_seqs=2, total_q_tokens=0, total_qblocks=0, max_pages_per_seq=0, max_mask_len=0)
+    assert L.cosa_osk_prefill(ctypes.byref(d0), *nul, 1.0, None, None, None, None, None, 0, None) == OK
+    assert binding.cosa_osk_check_args(good_dims(max_pages_per_seq=0), 1 << 20) == INVALID
+    bad = good_dims(num_seqs=2, total_q_tokens=0, total_qblocks=0, head_dim=64)
+    assert L.cosa_osk_prefill(ctypes.byref(bad), *nul, 1.0, None, None, None, None, None, 0, None) == UNSUPPORTED

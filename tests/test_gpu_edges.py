@@ -104,3 +104,25 @@ def test_widest_rows(rt):
     gpu = run(rt, bt, om, ml, delta)
     stats = check_prefill(bt, om, ml, delta, gpu)
     log("widest rows", stats)
+
+
+def test_empty_batch(rt):
+    """Every sequence empty (no query blocks, a page table of no columns): the prefill and the
+    mask builder launch nothing and return, with torch's empty tensors as arguments."""
+    import torch
+    from block_sparse_long_osk_amd import binding
+    wl = inputs.small_workload("empty_batch", [0, 0, 0], 4, 1, generator="structured", seed=5, pool="shuffled")
+    bt = inputs.generate(wl)
+    assert bt.total_qblocks == 0
+    log("empty batch: seq_lens", bt.workload.seq_lens, "page table", bt.page_table.shape)
+    db = rt.upload(bt)
+    om = np.zeros((0, 1, 4), dtype=np.int32)
+    ml = np.zeros((0, 1), dtype=np.int32)
+    omd, mld = rt.upload_mask(om, ml)
+    outs = rt.prefill(db, omd, mld, 100.0, log=True)
+    torch.cuda.synchronize()
+    assert tuple(outs.out.shape) == (0, 4, 128) and tuple(outs.decisions.shape) == (0, 4, 4)
+    bm, bl = rt.build_mask(db, 0.5, width=4)
+    torch.cuda.synchronize()
+    assert bm.shape[0] == 0 and bl.shape[0] == 0
+    assert binding.cosa_abi_version() == 2
